@@ -1,0 +1,93 @@
+"""The work-chunk rule of the host-side plan, written once here for the tests.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+The pages say only that planning inspects the sequence lengths and cache
+metadata, picks a schedule and prepares the workspace, and that a plan is
+reused while the geometry is unchanged (article "FlashInfer", section
+"Plan and run"), and that a fixed schedule can leave GPU work uneven (same
+article, section "Purpose and scope"). The exact rule below is this library's
+reading; the C++ planner implements the same rule independently and the tests
+require the two to agree item for item.
+
+Rule (all integer arithmetic; ceil(a / b) for b > 0):
+
+1.  Rows. Query rows are GQA-packed: row r of request b is query token r // G
+    and query head g * G + r % G of KV head g. A tile holds ``rows_per_tile``
+    consecutive rows (decode: rows_per_tile = G, one tile per request; prefill:
+    128 rows). Request b has tiles_b = ceil(Q_b * G / rows_per_tile).
+2.  KV extent of a tile. kv_end = L_b, or with the bottom-right causal mask
+    kv_end = clamp(L_b - Q_b + t_last + 1, 0, L_b), where t_last is the query
+    token of the tile's last row. pages = ceil(kv_end / P).
+3.  work = Hkv * sum over (b, tile) of pages.  target = num_cus * wg_per_cu.
+    c_min = max(1, ceil(min_chunk_tokens / P)).
+    c = max(c_min, ceil(work / target))   (c = c_min when work = 0).
+4.  Each (b, tile, g) group splits into n_chunks = max(1, ceil(pages / c))
+    chunks; chunk j covers pages [j*c, min((j+1)*c, pages)) and KV tokens
+    [j*c*P, min((j+1)*c*P, kv_end)). A group with one chunk writes its final
+    output; a group with more chunks writes partial states into consecutive
+    partial slots, assigned to split groups in (b, tile, g) order, chunk j at
+    slot_begin + j; those groups are listed, in the same order, as merge groups.
+5.  Items are executed longest first: sorted by descending KV token count,
+    ties broken by ascending (b, tile, g, j).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+@dataclass
+class PlanSpec:
+    chunk_pages: int
+    rows_per_tile: int
+    # (b, g, tile, page_begin, page_end, kv_begin, kv_end, slot) in execution order
+    items: list = field(default_factory=list)
+    # (b, tile, g, slot_begin, num_chunks) in (b, tile, g) order
+    merge_groups: list = field(default_factory=list)
+    num_slots: int = 0
+
+
+def plan_spec(qo_lens, kv_lens, page_size: int, num_kv_heads: int, group_size: int,
+              rows_per_tile: int, causal: bool, num_cus: int, wg_per_cu: int,
+              min_chunk_tokens: int) -> PlanSpec:
+    """Apply the rule in the module docstring. ``qo_lens`` / ``kv_lens`` per request."""
+    P, G = int(page_size), int(group_size)
+    B = len(kv_lens)
+    tiles = []   # (b, tile, kv_end, pages)
+    for b in range(B):
+        Q, L = int(qo_lens[b]), int(kv_lens[b])
+        n_rows = Q * G
+        for tile in range(_ceil_div(n_rows, rows_per_tile)):
+            last_row = min((tile + 1) * rows_per_tile, n_rows) - 1
+            t_last = last_row // G
+            kv_end = min(max(L - Q + t_last + 1, 0), L) if causal else L
+            tiles.append((b, tile, kv_end, _ceil_div(kv_end, P)))
+    work = num_kv_heads * sum(t[3] for t in tiles)
+    target = num_cus * wg_per_cu
+    c_min = max(1, _ceil_div(min_chunk_tokens, P))
+    c = max(c_min, _ceil_div(work, target))
+
+    spec = PlanSpec(chunk_pages=c, rows_per_tile=rows_per_tile)
+    raw = []      # (kv_count, b, tile, g, j, item)
+    slot = 0
+    for (b, tile, kv_end, pages) in tiles:           # (b, tile) order
+        n_chunks = max(1, _ceil_div(pages, c))
+        for g in range(num_kv_heads):                # then g
+            slot_begin = slot if n_chunks > 1 else -1
+            if n_chunks > 1:
+                spec.merge_groups.append((b, tile, g, slot_begin, n_chunks))
+                slot += n_chunks
+            for j in range(n_chunks):
+                p0, p1 = j * c, min((j + 1) * c, pages)
+                k0, k1 = min(j * c * P, kv_end), min((j + 1) * c * P, kv_end)
+                item = (b, g, tile, p0, p1, k0, k1, slot_begin + j if n_chunks > 1 else -1)
+                raw.append((k1 - k0, b, tile, g, j, item))
+    raw.sort(key=lambda r: (-r[0], r[1], r[2], r[3], r[4]))
+    spec.items = [r[5] for r in raw]
+    spec.num_slots = slot
+    return spec
