@@ -1,0 +1,306 @@
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+Default workload: batch paged decode, GQA (64 requests, KV length uniform in
+[512, 4096], 32 query / 8 KV heads, head_dim 128, fp16, 16-token pages, pool
+1.25x the pages needed). A step is one run of the planned pass (decode
+kernel plus the merge of split chunks) over the whole batch; the host plan is
+made once per workload before timing and reused, as the plan/run split
+intends, and its host time is reported as plan_us.
+
+Timing: W warm-up steps, then K timed steps. Before every step a 512 MiB
+buffer is overwritten (outside the timed events) so the 256 MB Infinity Cache
+holds no KV; each step is bracketed by HIP events on the stream the kernels
+run on. value = algorithmic bytes / mean step time.
+
+`--workload` selects another workload (single, decode, prefill, cascade,
+long); `--all` adds every workload's figures under "workloads" in the line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 / bf16 MFMA, TFLOP/s
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# algorithmic work (see the design doc for the per-unit figures)
+# ----------------------------------------------------------------------------
+def decode_bytes(kv_lens, Hkv, D, elem, B, Hq):
+    """K + V rows read once per (request, KV head), plus q, o and LSE."""
+    kv = int(np.sum(kv_lens)) * Hkv * D * elem * 2
+    return kv + B * Hq * D * elem * 2 + B * Hq * 4
+
+
+def prefill_flops(qo_lens, kv_lens, Hq, D, causal):
+    """4 * D * Hq * (number of visible (query, key) pairs)."""
+    pairs = 0
+    for Q, L in zip(qo_lens, kv_lens):
+        Q, L = int(Q), int(L)
+        if causal:
+            pre = L - Q
+            pairs += Q * pre + Q * (Q + 1) // 2
+        else:
+            pairs += Q * L
+    return 4.0 * D * Hq * pairs
+
+
+def prefill_bytes(w):
+    q = w.q.size * 2
+    kv = int(np.sum(w.kv.kv_lens)) * w.num_kv_heads * w.head_dim * 2 * 2
+    return q * 2 + kv + w.q.shape[0] * w.num_qo_heads * 4
+
+
+# ----------------------------------------------------------------------------
+# runners
+# ----------------------------------------------------------------------------
+class Runner:
+    """Uploads one workload, plans once, and exposes step() = one run."""
+
+    def __init__(self, name, w, pkv, torch):
+        self.name, self.w, self.pkv, self.torch = name, w, pkv, torch
+        dt = torch.float16 if w.dtype == "f16" else torch.bfloat16
+
+        def dev(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(dt).to("cuda")
+
+        def dev_i32(a):
+            a = np.asarray(a, np.int32)
+            return torch.from_numpy(a if a.size else np.zeros(1, np.int32)).to("cuda")
+
+        self.q = dev(w.q)
+        self.ws = pkv.Workspace()
+        if w.kind == "single_decode":
+            self.k, self.v = dev(w.k), dev(w.v)
+            self.o = torch.empty_like(self.q)
+            self.lse = torch.empty(self.q.shape[:1], dtype=torch.float32, device="cuda")
+        else:
+            self.k, self.v = dev(w.kv.k_cache), dev(w.kv.v_cache)
+            self.kv_indptr, self.kv_indices = dev_i32(w.kv.kv_indptr), dev_i32(w.kv.kv_indices)
+            self.o = torch.empty_like(self.q)
+            self.lse = torch.empty(self.q.shape[:2], dtype=torch.float32, device="cuda")
+            if w.kind == "prefill":
+                self.qo_indptr = dev_i32(w.qo_indptr)
+            if w.kind == "cascade":
+                self.prefix = dev_i32(w.prefix_indices)
+        self.dt = dt
+        self._plan()
+        # steady-state host plan time: the second plan of the same lengths
+        t0 = time.perf_counter()
+        self._plan()
+        self.plan_us = (time.perf_counter() - t0) * 1e6
+
+    def _plan(self):
+        w, pkv, torch, dt = self.w, self.pkv, self.torch, self.dt
+        if w.kind == "single_decode":
+            need = pkv._I64(0)
+            pkv._lib_single_decode(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(),
+                                   w.k.shape[0], w.num_qo_heads, w.num_kv_heads, w.head_dim,
+                                   pkv.dtype_code(dt), w.sm_scale, None, None, 0,
+                                   pkv.ctypes.byref(need), None, None, None)
+            self.fws = torch.empty(max(need.value, 16), dtype=torch.uint8, device="cuda")
+            self.plan = None
+        elif w.kind == "decode":
+            self.plan = pkv.pkv_decode_plan(w.kv.kv_indptr, w.kv.last_page_len, w.num_qo_heads,
+                                            w.num_kv_heads, w.head_dim, w.kv.page_size, dt,
+                                            self.ws)
+        elif w.kind == "prefill":
+            self.plan = pkv.pkv_prefill_plan(w.qo_indptr, w.kv.kv_indptr, w.kv.last_page_len,
+                                             w.num_qo_heads, w.num_kv_heads, w.head_dim,
+                                             w.kv.page_size, dt, w.causal, self.ws)
+        else:
+            self.plan = pkv.pkv_cascade_plan(len(w.prefix_indices), w.prefix_last_page_len,
+                                             w.kv.kv_indptr, w.kv.last_page_len, w.num_qo_heads,
+                                             w.num_kv_heads, w.head_dim, w.kv.page_size, dt,
+                                             self.ws)
+
+    def step(self):
+        p, w = self.pkv, self.w
+        if w.kind == "single_decode":
+            p.pkv_single_decode(self.q, self.k, self.v, w.sm_scale, float_ws=self.fws, o=self.o,
+                                lse=self.lse)
+        elif w.kind == "decode":
+            p.pkv_decode_run(self.plan, self.q, self.k, self.v, self.kv_indptr, self.kv_indices,
+                             w.sm_scale, o=self.o, lse=self.lse)
+        elif w.kind == "prefill":
+            p.pkv_prefill_run(self.plan, self.q, self.k, self.v, self.qo_indptr, self.kv_indptr,
+                              self.kv_indices, w.sm_scale, o=self.o, lse=self.lse)
+        else:
+            p.pkv_cascade_run(self.plan, self.q, self.k, self.v, self.prefix, self.kv_indptr,
+                              self.kv_indices, w.sm_scale, o=self.o, lse=self.lse)
+
+    def work(self):
+        """(algorithmic bytes, algorithmic flops, tokens) of one step."""
+        w = self.w
+        if w.kind == "single_decode":
+            L = w.k.shape[0]
+            b = decode_bytes([L], w.num_kv_heads, w.head_dim, 2, 1, w.num_qo_heads)
+            return b, 4.0 * w.num_qo_heads * w.head_dim * L, 1
+        if w.kind == "decode":
+            B = len(w.kv.kv_lens)
+            b = decode_bytes(w.kv.kv_lens, w.num_kv_heads, w.head_dim, 2, B, w.num_qo_heads)
+            return b, 4.0 * w.num_qo_heads * w.head_dim * float(np.sum(w.kv.kv_lens)), B
+        if w.kind == "prefill":
+            f = prefill_flops(w.meta["qo_lens"], w.kv.kv_lens, w.num_qo_heads, w.head_dim,
+                              w.causal)
+            return prefill_bytes(w), f, int(np.sum(w.meta["qo_lens"]))
+        B = len(w.kv.kv_lens)
+        pre = w.meta["prefix_len"]
+        suf = w.kv.kv_lens
+        b = (pre + int(np.sum(suf))) * w.num_kv_heads * w.head_dim * 2 * 2 + \
+            B * w.num_qo_heads * w.head_dim * 2 * 2 + B * w.num_qo_heads * 4
+        f = 4.0 * w.num_qo_heads * w.head_dim * B * pre + \
+            4.0 * w.num_qo_heads * w.head_dim * float(np.sum(suf))
+        return b, f, B
+
+
+def time_steps(torch, runner, steps, warmup, flush):
+    for _ in range(warmup):
+        flush.fill_(1)
+        runner.step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        flush.fill_(i & 0xFF)                # evicts the Infinity Cache, outside the events
+        starts[i].record(stream)
+        runner.step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return float(np.mean(ms)), float(np.median(ms)), wall
+
+
+def cpu_baseline(w, budget_s=15.0):
+    """The oracle as it stands on the host cores, on a bounded sample of requests."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    kv = w.kv
+    t0 = time.perf_counter()
+    done = []
+    for b in range(len(kv.kv_lens)):
+        oracle.batch_decode(w.q, kv.k_cache, kv.v_cache, kv.kv_indptr, kv.kv_indices,
+                            kv.last_page_len, w.dtype, w.sm_scale, requests=[b])
+        done.append(b)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    nbytes = decode_bytes(kv.kv_lens[done], w.num_kv_heads, w.head_dim, 2, len(done),
+                          w.num_qo_heads)
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 NumPy oracle over requests 0..{len(done) - 1} of the same batch "
+                      f"({len(done)} of {len(kv.kv_lens)} requests, all heads) in {dt:.1f} s"}
+
+
+WORKLOADS = {"single": 0, "decode": 1, "prefill": 2, "cascade": 3, "long": 4}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--all", action="store_true", help="also measure the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the path would shard requests or KV chunks across GPUs, see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from paged_kv_cache_173_amd import pkv
+    from paged_kv_cache_173_amd import workloads as wl
+
+    log(f"[bench] generating workload {args.workload}")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    names = [args.workload] + ([n for n in ("single", "decode", "prefill", "cascade", "long")
+                                if n != args.workload] if args.all else [])
+    results = {}
+    headline = None
+    for name in names:
+        w = wl.FULL[WORKLOADS[name]]()
+        r = Runner(name, w, pkv, torch)
+        log(f"[bench] {name}: planned in {r.plan_us:.0f} us; timing {args.steps} steps")
+        mean_ms, med_ms, wall = time_steps(torch, r, args.steps, args.warmup, flush)
+        nbytes, flops, tokens = r.work()
+        res = {"ms_per_step": mean_ms, "median_ms": med_ms, "plan_us": r.plan_us,
+               "GBps": nbytes / (mean_ms * 1e-3) / 1e9, "TFLOPs": flops / (mean_ms * 1e-3) / 1e12,
+               "tokens_per_s": tokens / (mean_ms * 1e-3), "bytes": nbytes, "flops": flops,
+               "wall_s": wall}
+        res["hbm_frac"] = res["GBps"] / HBM_PEAK_GBS
+        res["mfma_frac"] = res["TFLOPs"] / MFMA_PEAK_TFLOPS
+        log(f"[bench] {name}: {mean_ms * 1e3:.1f} us/step, {res['GBps']:.0f} GB/s "
+            f"({100 * res['hbm_frac']:.1f}% HBM), {res['TFLOPs']:.1f} TFLOP/s")
+        results[name] = res
+        if headline is None:
+            headline = (name, w, r, res)
+        else:
+            del r
+            torch.cuda.empty_cache()
+
+    name, w, r, res = headline
+    prefill_like = name == "prefill"
+    line = {
+        "metric": "paged decode HBM GB/s (% peak); prefill TFLOPS (% MFMA peak); tokens/s",
+        "value": res["TFLOPs"] if prefill_like else res["GBps"],
+        "unit": "TFLOP/s" if prefill_like else "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f16",
+        "data": "synthetic",
+        "config": {"workload": {
+            "single": "single-request decode, kv_len 1024, 32/32 heads, fp16, contiguous",
+            "decode": "batch paged decode, 64 requests, kv_len U[512,4096], 32/8 heads, P=16, fp16",
+            "prefill": "batch paged causal prefill, 16 requests, qo U[128,1024] after prefix "
+                       "U[0,2048], 32/8 heads, P=16, bf16",
+            "cascade": "cascade, 128 requests, 8192-token shared prefix, suffix U[64,1024], "
+                       "32/8 heads, P=16, fp16",
+            "long": "long-context split-KV decode, 4 x 131072 tokens, 64/8 heads, P=64, bf16",
+        }[name], "head_dim": 128, "tokens_per_step": r.work()[2],
+            "tokens_per_s": res["tokens_per_s"], "plan_us": res["plan_us"]},
+        "roofline": {
+            "bound": "mfma" if prefill_like else "hbm",
+            "achieved": res["TFLOPs"] if prefill_like else res["GBps"],
+            "peak": MFMA_PEAK_TFLOPS if prefill_like else HBM_PEAK_GBS,
+            "unit": "TFLOP/s" if prefill_like else "GB/s",
+            "frac": res["mfma_frac"] if prefill_like else res["hbm_frac"],
+            "traffic": None,
+        },
+    }
+    if len(results) > 1:
+        line["workloads"] = results
+    if not args.no_cpu_baseline and w.kind == "decode":
+        log("[bench] timing the CPU oracle on a bounded sample")
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

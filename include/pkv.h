@@ -1,0 +1,301 @@
+/*
+ * pkv.h -- C ABI of the MI355X paged-KV attention library (libpkv.so).
+ *
+ * What the library computes (the FlashInfer pages are the source):
+ *   - batched attention over a paged KV cache: the cache lives in fixed-size
+ *     pages that need not be contiguous, and a page table lists each
+ *     request's pages (article "FlashInfer", section "Block-sparse cache
+ *     representation"; docs index "KV-Cache Layout in FlashInfer" >
+ *     "Page Table Layout", "Layout: NHD/HND");
+ *   - decode (one query token per request) and causal prefill / append (many
+ *     query tokens per request appended after a cached prefix), exact
+ *     softmax attention with a running maximum (article "FlashInfer",
+ *     sections "Correctness and numerical behavior" and "Extreme-negative-logit
+ *     correction"; docs index "flashinfer.decode", "flashinfer.prefill");
+ *   - every output row comes with its log-sum-exp, forming an attention
+ *     state; states of disjoint KV parts merge into the state of their union
+ *     (article "FlashInfer", section "Attention states"; docs index
+ *     "flashinfer.cascade" > "Merge Attention States", "Cascade Attention");
+ *   - a host-side plan that inspects lengths and splits the KV into work
+ *     chunks, and a run that reuses the plan with stable workspace buffers
+ *     (article "FlashInfer", section "Plan and run").
+ *
+ * Conventions used by every entry point:
+ *   - Device pointers come from the caller (e.g. torch allocations); the
+ *     library never allocates or frees memory and keeps no pointer past the
+ *     call, except the workspace pointers a plan records (see pkv_plan_info).
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream). Run
+ *     and merge calls are asynchronous on that stream and do no host sync.
+ *   - Layouts are row-major and contiguous unless strides are given:
+ *       q, o     : decode [batch, num_qo_heads, head_dim],
+ *                  prefill [total_qo_tokens, num_qo_heads, head_dim];
+ *       lse      : float32, natural log, [rows, num_qo_heads];
+ *       KV pages : NHD, element (page, slot, kv_head, d) at
+ *                  base + page*page_stride + slot*token_stride + kv_head*head_stride + d.
+ *   - Page tables are int32: kv_indptr[batch+1] (monotone), kv_indices[...]
+ *     (page ids), last_page_len[batch] (1..page_size for a request with
+ *     pages, 0 for a request with none). Request b holds
+ *     L_b = (n_b-1)*page_size + last_page_len[b] tokens, token t at page
+ *     kv_indices[kv_indptr[b] + t/page_size], slot t%page_size.
+ *   - GQA: query head h reads KV head h / G, G = num_qo_heads / num_kv_heads.
+ *   - A row that sees no key (empty request, fully masked row) yields O = 0
+ *     and LSE = -inf; -inf is never replaced by a finite sentinel.
+ *   - Errors: every entry point returns a pkv_status; on failure nothing is
+ *     launched and pkv_last_error() returns a thread-local message.
+ *
+ * Supported today: head_dim 128; fp16 and bf16 storage; fp32 accumulation.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+typedef int32_t pkv_status;
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,         /* malformed argument (pointer, length, table)   */
+  PKV_ERR_UNSUPPORTED = 2,         /* well-formed but not implemented (head_dim...)  */
+  PKV_ERR_WORKSPACE_TOO_SMALL = 3, /* required sizes are reported in pkv_plan_info   */
+  PKV_ERR_PLAN_MISMATCH = 4,       /* plan does not belong to this call's geometry   */
+  PKV_ERR_HIP = 5                  /* a HIP runtime call failed                      */
+};
+
+typedef int32_t pkv_dtype;
+enum { PKV_F16 = 0, PKV_BF16 = 1, PKV_F32 = 2 };
+
+typedef int32_t pkv_kind;
+enum { PKV_KIND_DECODE = 1, PKV_KIND_PREFILL = 2, PKV_KIND_CASCADE = 3 };
+
+/* A paged K/V cache. k and v are separate device bases with one set of
+ * strides (in elements), which also covers an interleaved [pages, 2, P, H, D]
+ * pool. head_dim elements of one (page, slot, head) are contiguous. All
+ * strides must be multiples of 8 elements and k, v 16-byte aligned. */
+typedef struct pkv_paged_kv {
+  const void* k;
+  const void* v;
+  int64_t page_stride;
+  int64_t token_stride;
+  int64_t head_stride;
+  int32_t page_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  pkv_dtype dtype; /* PKV_F16 or PKV_BF16 */
+} pkv_paged_kv;
+
+/* Inputs of the work-chunk rule (see pkv_decode_plan). NULL means
+ * pkv_default_sched() of the current device. */
+typedef struct pkv_sched {
+  int32_t num_cus;          /* compute units the work is spread over          */
+  int32_t wg_per_cu;        /* work items per CU the chunk size aims for       */
+  int32_t min_chunk_tokens; /* no chunk is shorter than this (rounded to pages) */
+} pkv_sched;
+
+/* One planned pass (decode, prefill, or one level of a cascade). Offsets are
+ * in bytes from the workspace bases recorded in pkv_plan_info. */
+typedef struct pkv_plan_part {
+  int32_t num_items;        /* work items = workgroups launched              */
+  int32_t num_groups;       /* (request, tile, kv head) groups that split     */
+  int32_t chunk_pages;      /* chunk size c of the rule, in pages             */
+  int32_t rows_per_tile;    /* query rows per item (G for decode, 128 prefill) */
+  int32_t num_slots;        /* partial states written by split groups         */
+  int32_t causal;
+  int64_t items_off;        /* int ws: int32 [num_items][8]                   */
+  int64_t groups_off;       /* int ws: int32 [num_groups][8]                  */
+  int64_t kv_len_off;       /* int ws: int32 [batch] KV length per request    */
+  int64_t part_o_off;       /* float ws: f32 [num_slots][rows_per_tile][D]    */
+  int64_t part_lse_off;     /* float ws: f32 [num_slots][rows_per_tile]       */
+} pkv_plan_part;
+
+/* A plan: a plain struct the caller owns (copyable, no pointers to free).
+ * Valid for any run with the same lengths, heads, page size and dtype, as
+ * long as the recorded workspaces stay allocated at the same addresses. */
+typedef struct pkv_plan_info {
+  uint32_t magic;
+  int32_t abi_version;
+  pkv_kind kind;
+  pkv_dtype dtype;
+  int32_t batch;
+  int32_t num_qo_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t total_qo;          /* prefill: sum of query lengths; decode: batch */
+  pkv_sched sched;
+  void* int_ws;              /* device int workspace the plan was copied to  */
+  void* float_ws;            /* device float workspace for partial states    */
+  int64_t int_ws_required;   /* bytes (also set on WORKSPACE_TOO_SMALL)      */
+  int64_t float_ws_required; /* bytes (also set on WORKSPACE_TOO_SMALL)      */
+  int64_t cascade_state_off; /* cascade: float ws offset of the two fp32 states */
+  pkv_plan_part part[2];     /* part[0]: the pass; cascade: [0] prefix, [1] suffix */
+} pkv_plan_info;
+
+/* Thread-local message of the last failure on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* PKV_ABI_VERSION of the loaded library. */
+int32_t pkv_abi_version(void);
+
+/* sizeof(pkv_plan_info) as compiled into the library (lets a foreign-function
+ * binding check its mirror of the struct). */
+size_t pkv_plan_info_size(void);
+
+/* Fill *out with defaults for `device`: num_cus = the device's CU count,
+ * wg_per_cu = 4, min_chunk_tokens = 256. Needs a GPU. */
+pkv_status pkv_default_sched(int32_t device, pkv_sched* out);
+
+/* Defaults tuned to one kernel: as pkv_default_sched, but wg_per_cu is the
+ * number of workgroups of that kind's kernel resident on one CU (decode:
+ * the decode kernel; prefill: the prefill kernel), so one wave of workgroups
+ * covers the chip. A plan given a NULL sched uses this for its own kind (the
+ * cascade: prefill for level 0, decode for level 1). Needs a GPU. */
+pkv_status pkv_default_sched_for(pkv_kind kind, int32_t device, pkv_sched* out);
+
+/* ---------------------------------------------------------------------------
+ * Host-only planning (no GPU needed): the work-chunk rule.
+ *
+ * Rule (integer arithmetic, ceil(a/b) rounding up):
+ *   rows of request b are GQA-packed (row r = query token r/G, head
+ *   g*G + r%G); a tile holds rows_per_tile rows (decode: G; prefill: 128);
+ *   a tile's KV extent is L_b, or with the causal mask
+ *   clamp(L_b - Q_b + t_last + 1, 0, L_b) (t_last = query token of its last
+ *   row); pages(tile) = ceil(extent / P);
+ *   work = Hkv * sum pages(tile); target = num_cus * wg_per_cu;
+ *   c = max(max(1, ceil(min_chunk_tokens / P)), ceil(work / target));
+ *   each (b, tile, g) group splits into max(1, ceil(pages / c)) chunks, chunk
+ *   j covering pages [j*c, min((j+1)*c, pages)) and tokens
+ *   [j*c*P, min((j+1)*c*P, extent)); split groups get consecutive partial
+ *   slots in (b, tile, g) order; items run longest first (descending token
+ *   count, ties by ascending b, tile, g, j).
+ * Outputs: items_out[num_items][8] = {b, g, tile, page_begin, page_end,
+ *   kv_begin, kv_end, slot (-1 = writes the final output)};
+ *   groups_out[num_groups][8] = {b, tile, g, slot_begin, num_chunks, 0, 0, 0};
+ *   counts_out[4] = {num_items, num_groups, chunk_pages, num_slots}.
+ * qo_indptr_h may be NULL for decode (kind PKV_KIND_DECODE, one query token
+ * per request). Returns WORKSPACE_TOO_SMALL (counts still filled) when
+ * items_cap / groups_cap are too small.
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_plan_host(pkv_kind kind, const int32_t* qo_indptr_h, const int32_t* kv_indptr_h,
+                         const int32_t* last_page_len_h, int32_t batch, int32_t num_qo_heads,
+                         int32_t num_kv_heads, int32_t page_size, int32_t causal,
+                         const pkv_sched* sched, int32_t* items_out, int32_t items_cap,
+                         int32_t* groups_out, int32_t groups_cap, int32_t* counts_out);
+
+/* ---------------------------------------------------------------------------
+ * Batch paged decode: one query token per request.
+ *
+ * plan: validates the host page-table copies, applies the rule above, writes
+ * the item and group tables into host_ws (pinned memory recommended) and
+ * copies them to int_ws on `stream`, then waits for that copy (so host_ws is
+ * reusable on return). With int_ws / float_ws NULL or too small it returns
+ * WORKSPACE_TOO_SMALL and reports the required sizes in *out.
+ * run: checks that the plan matches `kv` and launches the decode kernel and,
+ * if any group split, the merge kernel. q [batch, Hq, 128], o like q
+ * (same dtype as the cache), lse [batch, Hq] float32 or NULL.
+ * sm_scale multiplies q.k (usually 1/sqrt(head_dim)).
+ * Needs 1 <= G <= 16.
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_decode_plan(const int32_t* kv_indptr_h, const int32_t* last_page_len_h,
+                           int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t page_size, pkv_dtype dtype,
+                           const pkv_sched* sched, void* int_ws, size_t int_ws_bytes,
+                           void* float_ws, size_t float_ws_bytes, void* host_ws,
+                           size_t host_ws_bytes, void* stream, pkv_plan_info* out);
+
+pkv_status pkv_decode_run(const pkv_plan_info* plan, const void* q, const pkv_paged_kv* kv,
+                          const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
+                          float sm_scale, void* o, float* lse, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Batch paged prefill / append: Q_b = qo_indptr[b+1]-qo_indptr[b] query
+ * tokens per request, the last Q_b of its L_b keys. causal=1 applies the
+ * bottom-right mask: query i sees key t iff t <= i + L_b - Q_b (rows with no
+ * visible key give O = 0, LSE = -inf). causal=0 lets every query see all L_b
+ * keys. q / o [total_qo, Hq, 128], lse [total_qo, Hq] float32 or NULL.
+ * Plan and workspace rules as for decode. Needs G <= 128.
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_prefill_plan(const int32_t* qo_indptr_h, const int32_t* kv_indptr_h,
+                            const int32_t* last_page_len_h, int32_t batch, int32_t num_qo_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                            pkv_dtype dtype, int32_t causal, const pkv_sched* sched, void* int_ws,
+                            size_t int_ws_bytes, void* float_ws, size_t float_ws_bytes,
+                            void* host_ws, size_t host_ws_bytes, void* stream,
+                            pkv_plan_info* out);
+
+pkv_status pkv_prefill_run(const pkv_plan_info* plan, const void* q, const pkv_paged_kv* kv,
+                           const int32_t* qo_indptr_d, const int32_t* kv_indptr_d,
+                           const int32_t* kv_indices_d, float sm_scale, void* o, float* lse,
+                           void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Single-request decode over a contiguous NHD cache k, v [kv_len, Hkv, 128]
+ * (token stride Hkv*128): q [Hq, 128] -> o [Hq, 128], lse [Hq] or NULL.
+ * The same chunk rule runs on the host with no device tables: chunks are
+ * uniform so items are derived from the workgroup index. float_ws must hold
+ * the partial states: Hq * (128 + 1) * 4 * ceil(kv_len / (c*16)) bytes at
+ * most, reported via float_ws_required when too small (pass NULL, 0 to
+ * query). The contiguous cache is handled as 16-token pages.
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_single_decode(const void* q, const void* k, const void* v, int32_t kv_len,
+                             int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                             pkv_dtype dtype, float sm_scale, const pkv_sched* sched,
+                             void* float_ws, size_t float_ws_bytes, int64_t* float_ws_required,
+                             void* o, float* lse, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Attention-state merges (docs index "Merge Attention States"). For each
+ * row: s* = max_k s_k; w_k = exp(s_k - s*); O = sum w_k v_k / sum w_k;
+ * LSE = s* + ln(sum w_k); if every s_k is -inf the result is (0, -inf).
+ * v_dtype is the dtype of every v array (F16, BF16 or F32); s arrays are
+ * float32 natural-log LSEs. Rows are (n, H) pairs of head_dim values.
+ * ------------------------------------------------------------------------- */
+/* (va, sa) + (vb, sb) -> (vo, so); va, vb, vo [n, H, D]; sa, sb, so [n, H]. */
+pkv_status pkv_merge_state(const void* va, const float* sa, const void* vb, const float* sb,
+                           void* vo, float* so, int32_t n, int32_t num_heads, int32_t head_dim,
+                           pkv_dtype v_dtype, void* stream);
+
+/* (v, s) <- merge((v, s), (v_other, s_other)), in place. */
+pkv_status pkv_merge_state_in_place(void* v, float* s, const void* v_other,
+                                    const float* s_other, int32_t n, int32_t num_heads,
+                                    int32_t head_dim, pkv_dtype v_dtype, void* stream);
+
+/* v [n, K, H, D], s [n, K, H] -> vo [n, H, D], so [n, H]; states merge in
+ * ascending k, so results are reproducible bit for bit. */
+pkv_status pkv_merge_states(const void* v, const float* s, int32_t n, int32_t num_states,
+                            int32_t num_heads, int32_t head_dim, pkv_dtype v_dtype, void* vo,
+                            float* so, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Two-level cascade decode (docs index "Cascade Attention",
+ * "Multi-level Cascade Inference Data Layout"): `batch` decode requests share
+ * one prefix page list (prefix_indices_h/_d, prefix_num_pages pages, the last
+ * holding prefix_last_page_len tokens) and each has its own suffix page table.
+ * Level 0 computes every request's state over the prefix in one pass that
+ * reads the prefix once (all batch*Hq query rows against it, unmasked);
+ * level 1 computes the state over each suffix (batch decode); the two states
+ * are merged into o [batch, Hq, 128] (cache dtype) and lse [batch, Hq] or NULL.
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_cascade_plan(int32_t prefix_num_pages, int32_t prefix_last_page_len,
+                            const int32_t* suffix_indptr_h, const int32_t* suffix_last_page_len_h,
+                            int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t page_size, pkv_dtype dtype,
+                            const pkv_sched* sched, void* int_ws, size_t int_ws_bytes,
+                            void* float_ws, size_t float_ws_bytes, void* host_ws,
+                            size_t host_ws_bytes, void* stream, pkv_plan_info* out);
+
+pkv_status pkv_cascade_run(const pkv_plan_info* plan, const void* q, const pkv_paged_kv* kv,
+                           const int32_t* prefix_indices_d, const int32_t* suffix_indptr_d,
+                           const int32_t* suffix_indices_d, float sm_scale, void* o, float* lse,
+                           void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,775 @@
+// C ABI of libpkv.so (declared in include/pkv.h): argument validation, the
+// host plan, workspace layout, the plan's host-to-device copy, and kernel
+// launches. Plan/run split, stable workspaces and reuse of a plan follow the
+// FlashInfer article, section "Plan and run".
+#include "pkv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "planner.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+constexpr uint32_t kPlanMagic = 0x31564b50u;  // "PKV1"
+constexpr int64_t kAlign = 256;
+constexpr int32_t kRowsPerPrefillTile = 128;
+constexpr int32_t kMaxDecodeGroup = 16;
+
+pkv_status fail(pkv_status st, const std::string& msg) {
+  g_error = msg;
+  return st;
+}
+
+pkv_status ok() {
+  g_error.clear();
+  return PKV_OK;
+}
+
+int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+pkv_status hip_fail(hipError_t e, const char* what) {
+  return fail(PKV_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+pkv_status check_heads(int32_t num_qo_heads, int32_t num_kv_heads) {
+  if (num_qo_heads <= 0 || num_kv_heads <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_qo_heads and num_kv_heads must be positive");
+  if (num_qo_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_qo_heads must be a multiple of num_kv_heads");
+  return PKV_OK;
+}
+
+pkv_status check_head_dim_dtype(int32_t head_dim, pkv_dtype dtype) {
+  if (head_dim <= 0) return fail(PKV_ERR_INVALID_ARG, "head_dim must be positive");
+  if (head_dim != pkv::kHeadDimSupported)
+    return fail(PKV_ERR_UNSUPPORTED, "only head_dim 128 is implemented");
+  if (dtype != PKV_F16 && dtype != PKV_BF16)
+    return fail(dtype == PKV_F32 ? PKV_ERR_UNSUPPORTED : PKV_ERR_INVALID_ARG,
+                "attention storage dtype must be PKV_F16 or PKV_BF16");
+  return PKV_OK;
+}
+
+pkv_status check_sched(const pkv_sched* s) {
+  if (s->num_cus <= 0 || s->wg_per_cu <= 0 || s->min_chunk_tokens <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "sched fields must be positive");
+  return PKV_OK;
+}
+
+pkv_status resolve_sched(const pkv_sched* in, pkv_kind kind, pkv_sched* out) {
+  if (in != nullptr) {
+    *out = *in;
+    return check_sched(out);
+  }
+  int32_t dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  return pkv_default_sched_for(kind, dev, out);
+}
+
+// Page table on the host: monotone indptr, last_page_len within [1, P] for a
+// request with pages and 0 for an empty one. Fills per-request KV lengths.
+pkv_status check_page_table(const int32_t* kv_indptr, const int32_t* last_page_len,
+                            int32_t batch, int32_t page_size, std::vector<int64_t>* kv_lens) {
+  if (batch < 0) return fail(PKV_ERR_INVALID_ARG, "batch must be >= 0");
+  if (page_size <= 0) return fail(PKV_ERR_INVALID_ARG, "page_size must be positive");
+  if (kv_indptr == nullptr || (batch > 0 && last_page_len == nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "kv_indptr / last_page_len host arrays are NULL");
+  if (kv_indptr[0] < 0) return fail(PKV_ERR_INVALID_ARG, "kv_indptr[0] must be >= 0");
+  kv_lens->resize(batch);
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t n = static_cast<int64_t>(kv_indptr[b + 1]) - kv_indptr[b];
+    if (n < 0) return fail(PKV_ERR_INVALID_ARG, "kv_indptr is not monotone at " + std::to_string(b));
+    const int32_t lpl = last_page_len[b];
+    if (n == 0) {
+      if (lpl != 0)
+        return fail(PKV_ERR_INVALID_ARG,
+                    "last_page_len must be 0 for request " + std::to_string(b) + " with no pages");
+      (*kv_lens)[b] = 0;
+    } else {
+      if (lpl < 1 || lpl > page_size)
+        return fail(PKV_ERR_INVALID_ARG, "last_page_len[" + std::to_string(b) +
+                                             "] must be in [1, page_size]");
+      const int64_t L = (n - 1) * page_size + lpl;
+      if (L > INT32_MAX) return fail(PKV_ERR_INVALID_ARG, "KV length overflows int32");
+      (*kv_lens)[b] = L;
+    }
+  }
+  return PKV_OK;
+}
+
+pkv_status check_qo_indptr(const int32_t* qo_indptr, int32_t batch, std::vector<int64_t>* qo_lens) {
+  if (qo_indptr == nullptr) return fail(PKV_ERR_INVALID_ARG, "qo_indptr host array is NULL");
+  if (qo_indptr[0] < 0) return fail(PKV_ERR_INVALID_ARG, "qo_indptr[0] must be >= 0");
+  qo_lens->resize(batch);
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t q = static_cast<int64_t>(qo_indptr[b + 1]) - qo_indptr[b];
+    if (q < 0) return fail(PKV_ERR_INVALID_ARG, "qo_indptr is not monotone at " + std::to_string(b));
+    (*qo_lens)[b] = q;
+  }
+  return PKV_OK;
+}
+
+pkv_status check_kv(const pkv_paged_kv* kv, const pkv_plan_info* plan) {
+  if (kv == nullptr || kv->k == nullptr || kv->v == nullptr)
+    return fail(PKV_ERR_INVALID_ARG, "paged KV (or its k / v pointer) is NULL");
+  if (kv->page_size != plan->page_size || kv->num_kv_heads != plan->num_kv_heads ||
+      kv->head_dim != plan->head_dim || kv->dtype != plan->dtype)
+    return fail(PKV_ERR_PLAN_MISMATCH, "paged KV geometry / dtype differs from the plan's");
+  if (kv->page_stride % 8 || kv->token_stride % 8 || kv->head_stride % 8 || kv->page_stride < 0 ||
+      kv->token_stride < 0 || kv->head_stride < 0)
+    return fail(PKV_ERR_INVALID_ARG, "KV strides must be non-negative multiples of 8 elements");
+  if (!aligned16(kv->k) || !aligned16(kv->v))
+    return fail(PKV_ERR_INVALID_ARG, "k / v must be 16-byte aligned");
+  if (kv->token_stride < kv->head_dim || kv->token_stride > (INT32_MAX / 32))
+    return fail(PKV_ERR_INVALID_ARG, "token_stride must be in [head_dim, 2^26)");
+  return PKV_OK;
+}
+
+pkv_status check_plan(const pkv_plan_info* plan, pkv_kind kind) {
+  if (plan == nullptr) return fail(PKV_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->magic != kPlanMagic || plan->abi_version != PKV_ABI_VERSION)
+    return fail(PKV_ERR_PLAN_MISMATCH, "not a plan made by this library version");
+  if (plan->kind != kind) return fail(PKV_ERR_PLAN_MISMATCH, "plan kind differs from this call");
+  return PKV_OK;
+}
+
+struct Layout {
+  int64_t int_bytes = 0;
+  int64_t float_bytes = 0;
+};
+
+// Places one part's tables and partial states at the current end of each workspace.
+void place_part(const pkv::HostPlan& hp, int64_t batch, int32_t rows_per_tile, int32_t causal,
+                Layout* lay, pkv_plan_part* part) {
+  part->num_items = static_cast<int32_t>(hp.items.size());
+  part->num_groups = static_cast<int32_t>(hp.groups.size());
+  part->chunk_pages = hp.chunk_pages;
+  part->rows_per_tile = rows_per_tile;
+  part->num_slots = hp.num_slots;
+  part->causal = causal;
+  part->items_off = lay->int_bytes;
+  lay->int_bytes = align_up(lay->int_bytes + static_cast<int64_t>(hp.items.size()) * 32);
+  part->groups_off = lay->int_bytes;
+  lay->int_bytes = align_up(lay->int_bytes + static_cast<int64_t>(hp.groups.size()) * 32);
+  part->kv_len_off = lay->int_bytes;
+  lay->int_bytes = align_up(lay->int_bytes + batch * 4);
+  part->part_o_off = lay->float_bytes;
+  lay->float_bytes = align_up(lay->float_bytes + static_cast<int64_t>(hp.num_slots) *
+                                                     rows_per_tile * pkv::kHeadDimSupported * 4);
+  part->part_lse_off = lay->float_bytes;
+  lay->float_bytes =
+      align_up(lay->float_bytes + static_cast<int64_t>(hp.num_slots) * rows_per_tile * 4);
+}
+
+void write_part(const pkv::HostPlan& hp, const std::vector<int64_t>& kv_lens,
+                const pkv_plan_part& part, char* host) {
+  int32_t* lens = reinterpret_cast<int32_t*>(host + part.kv_len_off);
+  for (size_t b = 0; b < kv_lens.size(); ++b) lens[b] = static_cast<int32_t>(kv_lens[b]);
+  if (!hp.items.empty())
+    std::memcpy(host + part.items_off, hp.items.data(), hp.items.size() * sizeof(pkv::PlanItem));
+  if (!hp.groups.empty())
+    std::memcpy(host + part.groups_off, hp.groups.data(),
+                hp.groups.size() * sizeof(pkv::MergeGroup));
+}
+
+// Checks the workspaces, then copies host_ws[0:int_bytes] to int_ws on the
+// stream and waits for the copy.
+pkv_status commit_plan(const Layout& lay, void* int_ws, size_t int_ws_bytes, void* float_ws,
+                       size_t float_ws_bytes, void* host_ws, size_t host_ws_bytes,
+                       hipStream_t stream, pkv_plan_info* out) {
+  out->int_ws_required = lay.int_bytes;
+  out->float_ws_required = lay.float_bytes;
+  if ((lay.int_bytes > 0 && (int_ws == nullptr || int_ws_bytes < static_cast<size_t>(lay.int_bytes))) ||
+      (lay.float_bytes > 0 &&
+       (float_ws == nullptr || float_ws_bytes < static_cast<size_t>(lay.float_bytes))) ||
+      (lay.int_bytes > 0 &&
+       (host_ws == nullptr || host_ws_bytes < static_cast<size_t>(lay.int_bytes))))
+    return fail(PKV_ERR_WORKSPACE_TOO_SMALL,
+                "workspace too small: need int " + std::to_string(lay.int_bytes) + " B, float " +
+                    std::to_string(lay.float_bytes) + " B, host " + std::to_string(lay.int_bytes) +
+                    " B");
+  if (!aligned16(int_ws) || !aligned16(float_ws))
+    return fail(PKV_ERR_INVALID_ARG, "workspaces must be 16-byte aligned");
+  out->int_ws = int_ws;
+  out->float_ws = float_ws;
+  if (lay.int_bytes > 0) {
+    hipError_t e = hipMemcpyAsync(int_ws, host_ws, lay.int_bytes, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan)");
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize(plan)");
+  }
+  return PKV_OK;
+}
+
+void fill_header(pkv_plan_info* out, pkv_kind kind, pkv_dtype dtype, int32_t batch, int32_t hq,
+                 int32_t hkv, int32_t head_dim, int32_t page_size, int32_t total_qo,
+                 const pkv_sched& sched) {
+  std::memset(out, 0, sizeof(*out));
+  out->magic = kPlanMagic;
+  out->abi_version = PKV_ABI_VERSION;
+  out->kind = kind;
+  out->dtype = dtype;
+  out->batch = batch;
+  out->num_qo_heads = hq;
+  out->num_kv_heads = hkv;
+  out->head_dim = head_dim;
+  out->page_size = page_size;
+  out->total_qo = total_qo;
+  out->sched = sched;
+}
+
+pkv::PlanInput make_input(const std::vector<int64_t>& qo, const std::vector<int64_t>& kv,
+                          int32_t page_size, int32_t hkv, int32_t G, int32_t rows, bool causal,
+                          const pkv_sched& s) {
+  pkv::PlanInput in{};
+  in.qo_lens = qo.data();
+  in.kv_lens = kv.data();
+  in.batch = static_cast<int32_t>(kv.size());
+  in.page_size = page_size;
+  in.num_kv_heads = hkv;
+  in.group_size = G;
+  in.rows_per_tile = rows;
+  in.causal = causal;
+  in.num_cus = s.num_cus;
+  in.wg_per_cu = s.wg_per_cu;
+  in.min_chunk_tokens = s.min_chunk_tokens;
+  return in;
+}
+
+pkv::PageMode page_mode(int32_t page_size) {
+  return page_size % 16 == 0 ? pkv::kPagedUniform : pkv::kPagedGeneric;
+}
+
+const char* ws_at(const void* base, int64_t off) { return static_cast<const char*>(base) + off; }
+float* f_at(void* base, int64_t off) {
+  return reinterpret_cast<float*>(static_cast<char*>(base) + off);
+}
+const int32_t* i_at(const void* base, int64_t off) {
+  return reinterpret_cast<const int32_t*>(ws_at(base, off));
+}
+
+// Launches one decode pass (items + merge) writing final rows to o / lse.
+pkv_status run_decode_part(const pkv_plan_info* plan, const pkv_plan_part& part, const void* q,
+                           const pkv_paged_kv* kv, const int32_t* kv_indptr_d,
+                           const int32_t* kv_indices_d, float sm_scale, void* o, float* lse,
+                           pkv::OutKind out_kind, hipStream_t stream) {
+  const int32_t G = plan->num_qo_heads / plan->num_kv_heads;
+  pkv::DecodeArgs a{};
+  a.q = q;
+  a.k = kv->k;
+  a.v = kv->v;
+  a.page_stride = kv->page_stride;
+  a.token_stride = kv->token_stride;
+  a.head_stride = kv->head_stride;
+  a.kv_indptr = kv_indptr_d;
+  a.kv_indices = kv_indices_d;
+  a.items = i_at(plan->int_ws, part.items_off);
+  a.page_size = plan->page_size;
+  a.num_qo_heads = plan->num_qo_heads;
+  a.group = G;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.o = o;
+  a.lse = lse;
+  a.part_o = f_at(plan->float_ws, part.part_o_off);
+  a.part_lse = f_at(plan->float_ws, part.part_lse_off);
+  hipError_t e = pkv::launch_decode(a, plan->dtype, out_kind, page_mode(plan->page_size),
+                                    part.num_items, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+  if (part.num_groups > 0) {
+    pkv::MergeGroupsArgs m{};
+    m.groups = i_at(plan->int_ws, part.groups_off);
+    m.rows_per_tile = part.rows_per_tile;
+    m.num_qo_heads = plan->num_qo_heads;
+    m.group = G;
+    m.prefill = 0;
+    m.part_o = a.part_o;
+    m.part_lse = a.part_lse;
+    m.o = o;
+    m.lse = lse;
+    e = pkv::launch_merge_groups(m, plan->dtype, out_kind, part.num_groups, stream);
+    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  }
+  return PKV_OK;
+}
+
+pkv_status run_prefill_part(const pkv_plan_info* plan, const pkv_plan_part& part, const void* q,
+                            const pkv_paged_kv* kv, const int32_t* qo_indptr_d,
+                            const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
+                            float sm_scale, void* o, float* lse, int32_t num_qo_heads,
+                            pkv::OutKind out_kind, hipStream_t stream) {
+  const int32_t G = num_qo_heads / plan->num_kv_heads;
+  pkv::PrefillArgs a{};
+  a.q = q;
+  a.k = kv->k;
+  a.v = kv->v;
+  a.page_stride = kv->page_stride;
+  a.token_stride = kv->token_stride;
+  a.head_stride = kv->head_stride;
+  a.qo_indptr = qo_indptr_d;
+  a.kv_indptr = kv_indptr_d;
+  a.kv_indices = kv_indices_d;
+  a.items = i_at(plan->int_ws, part.items_off);
+  a.kv_lens = i_at(plan->int_ws, part.kv_len_off);
+  a.page_size = plan->page_size;
+  a.num_qo_heads = num_qo_heads;
+  a.group = G;
+  a.causal = part.causal;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.o = o;
+  a.lse = lse;
+  a.part_o = f_at(plan->float_ws, part.part_o_off);
+  a.part_lse = f_at(plan->float_ws, part.part_lse_off);
+  hipError_t e = pkv::launch_prefill(a, plan->dtype, out_kind, page_mode(plan->page_size),
+                                     part.num_items, stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
+  if (part.num_groups > 0) {
+    pkv::MergeGroupsArgs m{};
+    m.groups = i_at(plan->int_ws, part.groups_off);
+    m.rows_per_tile = part.rows_per_tile;
+    m.num_qo_heads = num_qo_heads;
+    m.group = G;
+    m.prefill = 1;
+    m.qo_indptr = qo_indptr_d;
+    m.part_o = a.part_o;
+    m.part_lse = a.part_lse;
+    m.o = o;
+    m.lse = lse;
+    e = pkv::launch_merge_groups(m, plan->dtype, out_kind, part.num_groups, stream);
+    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  }
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_error.c_str(); }
+
+int32_t pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+size_t pkv_plan_info_size(void) { return sizeof(pkv_plan_info); }
+
+pkv_status pkv_default_sched(int32_t device, pkv_sched* out) {
+  if (out == nullptr) return fail(PKV_ERR_INVALID_ARG, "out is NULL");
+  int cus = 0;
+  hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(CU count)");
+  out->num_cus = cus;
+  out->wg_per_cu = 4;
+  out->min_chunk_tokens = 256;
+  return ok();
+}
+
+pkv_status pkv_default_sched_for(pkv_kind kind, int32_t device, pkv_sched* out) {
+  if (kind != PKV_KIND_DECODE && kind != PKV_KIND_PREFILL)
+    return fail(PKV_ERR_INVALID_ARG, "kind must be PKV_KIND_DECODE or PKV_KIND_PREFILL");
+  pkv_status st = pkv_default_sched(device, out);
+  if (st) return st;
+  int32_t cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+  const int32_t occ = kind == PKV_KIND_DECODE ? pkv::decode_occupancy() : pkv::prefill_occupancy();
+  if (cur != device) (void)hipSetDevice(cur);
+  if (occ > 0) out->wg_per_cu = occ;
+  return ok();
+}
+
+pkv_status pkv_plan_host(pkv_kind kind, const int32_t* qo_indptr_h, const int32_t* kv_indptr_h,
+                         const int32_t* last_page_len_h, int32_t batch, int32_t num_qo_heads,
+                         int32_t num_kv_heads, int32_t page_size, int32_t causal,
+                         const pkv_sched* sched, int32_t* items_out, int32_t items_cap,
+                         int32_t* groups_out, int32_t groups_cap, int32_t* counts_out) {
+  if (sched == nullptr) return fail(PKV_ERR_INVALID_ARG, "pkv_plan_host needs an explicit sched");
+  if (counts_out == nullptr) return fail(PKV_ERR_INVALID_ARG, "counts_out is NULL");
+  pkv_status st = check_sched(sched);
+  if (st) return st;
+  if ((st = check_heads(num_qo_heads, num_kv_heads))) return st;
+  if (kind != PKV_KIND_DECODE && kind != PKV_KIND_PREFILL)
+    return fail(PKV_ERR_INVALID_ARG, "kind must be PKV_KIND_DECODE or PKV_KIND_PREFILL");
+  std::vector<int64_t> kv_lens, qo_lens;
+  if ((st = check_page_table(kv_indptr_h, last_page_len_h, batch, page_size, &kv_lens))) return st;
+  const int32_t G = num_qo_heads / num_kv_heads;
+  int32_t rows;
+  if (kind == PKV_KIND_DECODE) {
+    qo_lens.assign(batch, 1);
+    rows = G;
+    causal = 0;
+  } else {
+    if ((st = check_qo_indptr(qo_indptr_h, batch, &qo_lens))) return st;
+    rows = kRowsPerPrefillTile;
+  }
+  pkv::HostPlan hp;
+  std::string err;
+  if (!pkv::build_plan(make_input(qo_lens, kv_lens, page_size, num_kv_heads, G, rows, causal != 0,
+                                  *sched),
+                       &hp, &err))
+    return fail(PKV_ERR_INVALID_ARG, err);
+  counts_out[0] = static_cast<int32_t>(hp.items.size());
+  counts_out[1] = static_cast<int32_t>(hp.groups.size());
+  counts_out[2] = hp.chunk_pages;
+  counts_out[3] = hp.num_slots;
+  if (static_cast<int64_t>(hp.items.size()) > items_cap ||
+      static_cast<int64_t>(hp.groups.size()) > groups_cap)
+    return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "items_cap / groups_cap too small");
+  if (!hp.items.empty()) {
+    if (items_out == nullptr) return fail(PKV_ERR_INVALID_ARG, "items_out is NULL");
+    std::memcpy(items_out, hp.items.data(), hp.items.size() * sizeof(pkv::PlanItem));
+  }
+  if (!hp.groups.empty()) {
+    if (groups_out == nullptr) return fail(PKV_ERR_INVALID_ARG, "groups_out is NULL");
+    std::memcpy(groups_out, hp.groups.data(), hp.groups.size() * sizeof(pkv::MergeGroup));
+  }
+  return ok();
+}
+
+pkv_status pkv_decode_plan(const int32_t* kv_indptr_h, const int32_t* last_page_len_h,
+                           int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t page_size, pkv_dtype dtype,
+                           const pkv_sched* sched, void* int_ws, size_t int_ws_bytes,
+                           void* float_ws, size_t float_ws_bytes, void* host_ws,
+                           size_t host_ws_bytes, void* stream, pkv_plan_info* out) {
+  if (out == nullptr) return fail(PKV_ERR_INVALID_ARG, "out is NULL");
+  pkv_status st;
+  if ((st = check_heads(num_qo_heads, num_kv_heads))) return st;
+  if ((st = check_head_dim_dtype(head_dim, dtype))) return st;
+  const int32_t G = num_qo_heads / num_kv_heads;
+  if (G > kMaxDecodeGroup)
+    return fail(PKV_ERR_UNSUPPORTED, "decode supports num_qo_heads / num_kv_heads <= 16");
+  std::vector<int64_t> kv_lens;
+  if ((st = check_page_table(kv_indptr_h, last_page_len_h, batch, page_size, &kv_lens))) return st;
+  pkv_sched s;
+  if ((st = resolve_sched(sched, PKV_KIND_DECODE, &s))) return st;
+  std::vector<int64_t> qo_lens(batch, 1);
+  pkv::HostPlan hp;
+  std::string err;
+  if (!pkv::build_plan(make_input(qo_lens, kv_lens, page_size, num_kv_heads, G, G, false, s), &hp,
+                       &err))
+    return fail(PKV_ERR_INVALID_ARG, err);
+  fill_header(out, PKV_KIND_DECODE, dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
+              batch, s);
+  Layout lay;
+  place_part(hp, batch, G, 0, &lay, &out->part[0]);
+  if (host_ws != nullptr && host_ws_bytes >= static_cast<size_t>(lay.int_bytes))
+    write_part(hp, kv_lens, out->part[0], static_cast<char*>(host_ws));
+  if ((st = commit_plan(lay, int_ws, int_ws_bytes, float_ws, float_ws_bytes, host_ws,
+                        host_ws_bytes, static_cast<hipStream_t>(stream), out)))
+    return st;
+  return ok();
+}
+
+pkv_status pkv_decode_run(const pkv_plan_info* plan, const void* q, const pkv_paged_kv* kv,
+                          const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
+                          float sm_scale, void* o, float* lse, void* stream) {
+  pkv_status st;
+  if ((st = check_plan(plan, PKV_KIND_DECODE))) return st;
+  if ((st = check_kv(kv, plan))) return st;
+  if (plan->batch > 0 && (q == nullptr || o == nullptr || kv_indptr_d == nullptr ||
+                          kv_indices_d == nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "q, o, kv_indptr or kv_indices is NULL");
+  if (!aligned16(q) || !aligned16(o)) return fail(PKV_ERR_INVALID_ARG, "q / o must be 16-byte aligned");
+  if ((st = run_decode_part(plan, plan->part[0], q, kv, kv_indptr_d, kv_indices_d, sm_scale, o,
+                            lse, pkv::kOutStorage, static_cast<hipStream_t>(stream))))
+    return st;
+  return ok();
+}
+
+pkv_status pkv_prefill_plan(const int32_t* qo_indptr_h, const int32_t* kv_indptr_h,
+                            const int32_t* last_page_len_h, int32_t batch, int32_t num_qo_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                            pkv_dtype dtype, int32_t causal, const pkv_sched* sched, void* int_ws,
+                            size_t int_ws_bytes, void* float_ws, size_t float_ws_bytes,
+                            void* host_ws, size_t host_ws_bytes, void* stream,
+                            pkv_plan_info* out) {
+  if (out == nullptr) return fail(PKV_ERR_INVALID_ARG, "out is NULL");
+  pkv_status st;
+  if ((st = check_heads(num_qo_heads, num_kv_heads))) return st;
+  if ((st = check_head_dim_dtype(head_dim, dtype))) return st;
+  if (causal != 0 && causal != 1) return fail(PKV_ERR_INVALID_ARG, "causal must be 0 or 1");
+  const int32_t G = num_qo_heads / num_kv_heads;
+  if (G > kRowsPerPrefillTile)
+    return fail(PKV_ERR_UNSUPPORTED, "prefill supports num_qo_heads / num_kv_heads <= 128");
+  std::vector<int64_t> kv_lens, qo_lens;
+  if ((st = check_page_table(kv_indptr_h, last_page_len_h, batch, page_size, &kv_lens))) return st;
+  if ((st = check_qo_indptr(qo_indptr_h, batch, &qo_lens))) return st;
+  int64_t total_qo = 0;
+  for (int64_t qn : qo_lens) total_qo += qn;
+  if (total_qo * num_qo_heads > INT32_MAX)
+    return fail(PKV_ERR_INVALID_ARG, "total query rows overflow int32");
+  pkv_sched s;
+  if ((st = resolve_sched(sched, PKV_KIND_PREFILL, &s))) return st;
+  pkv::HostPlan hp;
+  std::string err;
+  if (!pkv::build_plan(make_input(qo_lens, kv_lens, page_size, num_kv_heads, G,
+                                  kRowsPerPrefillTile, causal != 0, s),
+                       &hp, &err))
+    return fail(PKV_ERR_INVALID_ARG, err);
+  fill_header(out, PKV_KIND_PREFILL, dtype, batch, num_qo_heads, num_kv_heads, head_dim,
+              page_size, static_cast<int32_t>(total_qo), s);
+  Layout lay;
+  place_part(hp, batch, kRowsPerPrefillTile, causal, &lay, &out->part[0]);
+  if (host_ws != nullptr && host_ws_bytes >= static_cast<size_t>(lay.int_bytes))
+    write_part(hp, kv_lens, out->part[0], static_cast<char*>(host_ws));
+  if ((st = commit_plan(lay, int_ws, int_ws_bytes, float_ws, float_ws_bytes, host_ws,
+                        host_ws_bytes, static_cast<hipStream_t>(stream), out)))
+    return st;
+  return ok();
+}
+
+pkv_status pkv_prefill_run(const pkv_plan_info* plan, const void* q, const pkv_paged_kv* kv,
+                           const int32_t* qo_indptr_d, const int32_t* kv_indptr_d,
+                           const int32_t* kv_indices_d, float sm_scale, void* o, float* lse,
+                           void* stream) {
+  pkv_status st;
+  if ((st = check_plan(plan, PKV_KIND_PREFILL))) return st;
+  if ((st = check_kv(kv, plan))) return st;
+  if (plan->total_qo > 0 && (q == nullptr || o == nullptr || qo_indptr_d == nullptr ||
+                             kv_indptr_d == nullptr || kv_indices_d == nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "q, o, qo_indptr, kv_indptr or kv_indices is NULL");
+  if (!aligned16(q) || !aligned16(o)) return fail(PKV_ERR_INVALID_ARG, "q / o must be 16-byte aligned");
+  if ((st = run_prefill_part(plan, plan->part[0], q, kv, qo_indptr_d, kv_indptr_d, kv_indices_d,
+                             sm_scale, o, lse, plan->num_qo_heads, pkv::kOutStorage,
+                             static_cast<hipStream_t>(stream))))
+    return st;
+  return ok();
+}
+
+pkv_status pkv_single_decode(const void* q, const void* k, const void* v, int32_t kv_len,
+                             int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                             pkv_dtype dtype, float sm_scale, const pkv_sched* sched,
+                             void* float_ws, size_t float_ws_bytes, int64_t* float_ws_required,
+                             void* o, float* lse, void* stream) {
+  pkv_status st;
+  if ((st = check_heads(num_qo_heads, num_kv_heads))) return st;
+  if ((st = check_head_dim_dtype(head_dim, dtype))) return st;
+  if (kv_len < 0) return fail(PKV_ERR_INVALID_ARG, "kv_len must be >= 0");
+  const int32_t G = num_qo_heads / num_kv_heads;
+  if (G > kMaxDecodeGroup)
+    return fail(PKV_ERR_UNSUPPORTED, "decode supports num_qo_heads / num_kv_heads <= 16");
+  pkv_sched s;
+  if ((st = resolve_sched(sched, PKV_KIND_DECODE, &s))) return st;
+  // The contiguous cache is a run of 16-token pages; the plan rule picks c.
+  constexpr int32_t kVirtualPage = 16;
+  std::vector<int64_t> qo_lens(1, 1), kv_lens(1, kv_len);
+  pkv::HostPlan hp;
+  std::string err;
+  if (!pkv::build_plan(make_input(qo_lens, kv_lens, kVirtualPage, num_kv_heads, G, G, false, s),
+                       &hp, &err))
+    return fail(PKV_ERR_INVALID_ARG, err);
+  const int64_t n_pages = (static_cast<int64_t>(kv_len) + kVirtualPage - 1) / kVirtualPage;
+  const int64_t c = hp.chunk_pages;
+  const int32_t nchunks = static_cast<int32_t>(std::max<int64_t>(1, (n_pages + c - 1) / c));
+  const int64_t need =
+      nchunks > 1 ? align_up(static_cast<int64_t>(num_kv_heads) * nchunks * G * head_dim * 4) +
+                        static_cast<int64_t>(num_kv_heads) * nchunks * G * 4
+                  : 0;
+  if (float_ws_required != nullptr) *float_ws_required = need;
+  if (need > 0 && (float_ws == nullptr || float_ws_bytes < static_cast<size_t>(need)))
+    return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "float workspace too small: need " +
+                                                 std::to_string(need) + " B");
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr)
+    return fail(PKV_ERR_INVALID_ARG, "q, k, v or o is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(float_ws))
+    return fail(PKV_ERR_INVALID_ARG, "q, k, v, o and float_ws must be 16-byte aligned");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  pkv::DecodeArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.token_stride = static_cast<int64_t>(num_kv_heads) * head_dim;
+  a.head_stride = head_dim;
+  a.page_stride = a.token_stride * kVirtualPage;
+  a.items = nullptr;
+  a.implicit_nchunks = nchunks;
+  a.implicit_chunk_tokens = static_cast<int32_t>(c * kVirtualPage);
+  a.implicit_kv_len = kv_len;
+  a.page_size = kVirtualPage;
+  a.num_qo_heads = num_qo_heads;
+  a.group = G;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.o = o;
+  a.lse = lse;
+  float* part_o = static_cast<float*>(float_ws);
+  float* part_lse =
+      nchunks > 1 ? f_at(float_ws, align_up(static_cast<int64_t>(num_kv_heads) * nchunks * G *
+                                            head_dim * 4))
+                  : nullptr;
+  a.part_o = part_o;
+  a.part_lse = part_lse;
+  hipError_t e = pkv::launch_decode(a, dtype, pkv::kOutStorage, pkv::kContiguous,
+                                    num_kv_heads * nchunks, hs);
+  if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+  if (nchunks > 1) {
+    pkv::MergeGroupsArgs m{};
+    m.groups = nullptr;
+    m.implicit_nchunks = nchunks;
+    m.rows_per_tile = G;
+    m.num_qo_heads = num_qo_heads;
+    m.group = G;
+    m.prefill = 0;
+    m.part_o = part_o;
+    m.part_lse = part_lse;
+    m.o = o;
+    m.lse = lse;
+    e = pkv::launch_merge_groups(m, dtype, pkv::kOutStorage, num_kv_heads, hs);
+    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  }
+  return ok();
+}
+
+static pkv_status check_merge_args(int32_t n, int32_t num_heads, int32_t head_dim,
+                                   pkv_dtype v_dtype) {
+  if (n < 0 || num_heads <= 0 || head_dim <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "n must be >= 0, num_heads and head_dim positive");
+  if (v_dtype != PKV_F16 && v_dtype != PKV_BF16 && v_dtype != PKV_F32)
+    return fail(PKV_ERR_INVALID_ARG, "v_dtype must be PKV_F16, PKV_BF16 or PKV_F32");
+  return PKV_OK;
+}
+
+pkv_status pkv_merge_state(const void* va, const float* sa, const void* vb, const float* sb,
+                           void* vo, float* so, int32_t n, int32_t num_heads, int32_t head_dim,
+                           pkv_dtype v_dtype, void* stream) {
+  pkv_status st;
+  if ((st = check_merge_args(n, num_heads, head_dim, v_dtype))) return st;
+  if (n > 0 && (!va || !sa || !vb || !sb || !vo))
+    return fail(PKV_ERR_INVALID_ARG, "va, sa, vb, sb and vo must be non-NULL");
+  hipError_t e = pkv::launch_merge2(va, sa, vb, sb, vo, so, static_cast<int64_t>(n) * num_heads,
+                                    head_dim, v_dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  return ok();
+}
+
+pkv_status pkv_merge_state_in_place(void* v, float* s, const void* v_other, const float* s_other,
+                                    int32_t n, int32_t num_heads, int32_t head_dim,
+                                    pkv_dtype v_dtype, void* stream) {
+  pkv_status st;
+  if ((st = check_merge_args(n, num_heads, head_dim, v_dtype))) return st;
+  if (n > 0 && (!v || !s || !v_other || !s_other))
+    return fail(PKV_ERR_INVALID_ARG, "v, s, v_other and s_other must be non-NULL");
+  hipError_t e = pkv::launch_merge2(v, s, v_other, s_other, v, s,
+                                    static_cast<int64_t>(n) * num_heads, head_dim, v_dtype,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  return ok();
+}
+
+pkv_status pkv_merge_states(const void* v, const float* s, int32_t n, int32_t num_states,
+                            int32_t num_heads, int32_t head_dim, pkv_dtype v_dtype, void* vo,
+                            float* so, void* stream) {
+  pkv_status st;
+  if ((st = check_merge_args(n, num_heads, head_dim, v_dtype))) return st;
+  if (num_states < 0) return fail(PKV_ERR_INVALID_ARG, "num_states must be >= 0");
+  if (n > 0 && (!vo || (num_states > 0 && (!v || !s))))
+    return fail(PKV_ERR_INVALID_ARG, "v, s and vo must be non-NULL");
+  hipError_t e = pkv::launch_merge_n(v, s, n, num_states, num_heads, head_dim, v_dtype, vo, so,
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  return ok();
+}
+
+pkv_status pkv_cascade_plan(int32_t prefix_num_pages, int32_t prefix_last_page_len,
+                            const int32_t* suffix_indptr_h, const int32_t* suffix_last_page_len_h,
+                            int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t page_size, pkv_dtype dtype,
+                            const pkv_sched* sched, void* int_ws, size_t int_ws_bytes,
+                            void* float_ws, size_t float_ws_bytes, void* host_ws,
+                            size_t host_ws_bytes, void* stream, pkv_plan_info* out) {
+  if (out == nullptr) return fail(PKV_ERR_INVALID_ARG, "out is NULL");
+  pkv_status st;
+  if ((st = check_heads(num_qo_heads, num_kv_heads))) return st;
+  if ((st = check_head_dim_dtype(head_dim, dtype))) return st;
+  const int32_t G = num_qo_heads / num_kv_heads;
+  if (G > kMaxDecodeGroup)
+    return fail(PKV_ERR_UNSUPPORTED, "cascade decode supports num_qo_heads / num_kv_heads <= 16");
+  if (prefix_num_pages < 0) return fail(PKV_ERR_INVALID_ARG, "prefix_num_pages must be >= 0");
+  // Level 0: one "request" whose query tokens are the batch's decode tokens.
+  const int32_t pre_indptr[2] = {0, prefix_num_pages};
+  const int32_t pre_lpl[1] = {prefix_last_page_len};
+  std::vector<int64_t> pre_len, suf_len;
+  if ((st = check_page_table(pre_indptr, pre_lpl, 1, page_size, &pre_len))) return st;
+  if ((st = check_page_table(suffix_indptr_h, suffix_last_page_len_h, batch, page_size, &suf_len)))
+    return st;
+  pkv_sched s0, s1;
+  if ((st = resolve_sched(sched, PKV_KIND_PREFILL, &s0))) return st;
+  if ((st = resolve_sched(sched, PKV_KIND_DECODE, &s1))) return st;
+  std::vector<int64_t> pre_qo(1, batch), suf_qo(batch, 1);
+  pkv::HostPlan hp0, hp1;
+  std::string err;
+  if (!pkv::build_plan(make_input(pre_qo, pre_len, page_size, num_kv_heads, G,
+                                  kRowsPerPrefillTile, false, s0),
+                       &hp0, &err) ||
+      !pkv::build_plan(make_input(suf_qo, suf_len, page_size, num_kv_heads, G, G, false, s1), &hp1,
+                       &err))
+    return fail(PKV_ERR_INVALID_ARG, err);
+  fill_header(out, PKV_KIND_CASCADE, dtype, batch, num_qo_heads, num_kv_heads, head_dim,
+              page_size, batch, s1);
+  Layout lay;
+  // int ws: [level-0 qo_indptr (2), level-0 kv_indptr (2)] then both parts' tables
+  lay.int_bytes = kAlign;
+  place_part(hp0, 1, kRowsPerPrefillTile, 0, &lay, &out->part[0]);
+  place_part(hp1, batch, G, 0, &lay, &out->part[1]);
+  // float ws: both parts' partials, then fp32 states A (prefix) and B (suffix)
+  out->cascade_state_off = lay.float_bytes;
+  const int64_t rows = static_cast<int64_t>(batch) * num_qo_heads;
+  lay.float_bytes += 2 * (align_up(rows * head_dim * 4) + align_up(rows * 4));
+  if (host_ws != nullptr && host_ws_bytes >= static_cast<size_t>(lay.int_bytes)) {
+    char* h = static_cast<char*>(host_ws);
+    const int32_t hdr[4] = {0, batch, 0, prefix_num_pages};
+    std::memcpy(h, hdr, sizeof(hdr));
+    write_part(hp0, pre_len, out->part[0], h);
+    write_part(hp1, suf_len, out->part[1], h);
+  }
+  if ((st = commit_plan(lay, int_ws, int_ws_bytes, float_ws, float_ws_bytes, host_ws,
+                        host_ws_bytes, static_cast<hipStream_t>(stream), out)))
+    return st;
+  return ok();
+}
+
+pkv_status pkv_cascade_run(const pkv_plan_info* plan, const void* q, const pkv_paged_kv* kv,
+                           const int32_t* prefix_indices_d, const int32_t* suffix_indptr_d,
+                           const int32_t* suffix_indices_d, float sm_scale, void* o, float* lse,
+                           void* stream) {
+  pkv_status st;
+  if ((st = check_plan(plan, PKV_KIND_CASCADE))) return st;
+  if ((st = check_kv(kv, plan))) return st;
+  if (plan->batch == 0) return ok();
+  if (q == nullptr || o == nullptr || suffix_indptr_d == nullptr || suffix_indices_d == nullptr ||
+      (plan->part[0].num_items > 0 && prefix_indices_d == nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "q, o, prefix / suffix tables must be non-NULL");
+  if (!aligned16(q) || !aligned16(o)) return fail(PKV_ERR_INVALID_ARG, "q / o must be 16-byte aligned");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int64_t rows = static_cast<int64_t>(plan->batch) * plan->num_qo_heads;
+  const int64_t D = plan->head_dim;
+  float* a_o = f_at(plan->float_ws, plan->cascade_state_off);
+  float* a_lse = f_at(plan->float_ws, plan->cascade_state_off + align_up(rows * D * 4));
+  float* b_o = f_at(plan->float_ws,
+                    plan->cascade_state_off + align_up(rows * D * 4) + align_up(rows * 4));
+  float* b_lse = f_at(plan->float_ws, plan->cascade_state_off + 2 * align_up(rows * D * 4) +
+                                          align_up(rows * 4));
+  const int32_t* hdr = i_at(plan->int_ws, 0);
+  // Level 0: prefix state of every (request, head) row, prefix read once.
+  if ((st = run_prefill_part(plan, plan->part[0], q, kv, hdr, hdr + 2, prefix_indices_d, sm_scale,
+                             a_o, a_lse, plan->num_qo_heads, pkv::kOutF32, hs)))
+    return st;
+  // Level 1: suffix state per request (batch decode).
+  if ((st = run_decode_part(plan, plan->part[1], q, kv, suffix_indptr_d, suffix_indices_d,
+                            sm_scale, b_o, b_lse, pkv::kOutF32, hs)))
+    return st;
+  hipError_t e = pkv::launch_merge2_f32_to(a_o, a_lse, b_o, b_lse, o, lse, rows,
+                                           static_cast<int32_t>(D), plan->dtype, hs);
+  if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// Kernel argument blocks and host-side launchers (implemented in the .hip files).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace pkv {
+
+constexpr int32_t kHeadDimSupported = 128;
+
+// How a kernel finds the address of logical token t of a request.
+enum PageMode : int32_t {
+  kContiguous = 0,    // no page table: token t at t * token_stride
+  kPagedUniform = 1,  // page_size % 16 == 0: a 16-token block never straddles a page
+  kPagedGeneric = 2,  // any page_size: one page-table lookup per lane and token
+};
+
+enum OutKind : int32_t { kOutStorage = 0, kOutF32 = 1 };
+
+struct DecodeArgs {
+  const void* q;            // [batch, Hq, 128] storage dtype
+  const void* k;            // K page pool base
+  const void* v;            // V page pool base
+  int64_t page_stride, token_stride, head_stride;  // elements
+  const int32_t* kv_indptr;   // device [batch+1] (paged modes)
+  const int32_t* kv_indices;  // device page ids (paged modes)
+  const int32_t* items;       // device [num_items][8], or NULL: implicit uniform chunks
+  int32_t implicit_nchunks;   // implicit mode: chunks per KV head (single request)
+  int32_t implicit_chunk_tokens;
+  int32_t implicit_kv_len;
+  int32_t page_size;
+  int32_t num_qo_heads;
+  int32_t group;              // G <= 16
+  float scale_log2;           // sm_scale * log2(e)
+  void* o;                    // final output rows [batch*Hq][128]
+  float* lse;                 // final LSE [batch*Hq] or NULL
+  float* part_o;              // partial states [slot][G][128]
+  float* part_lse;            // [slot][G]
+};
+
+struct PrefillArgs {
+  const void* q;            // [total_qo, Hq, 128] storage dtype
+  const void* k;
+  const void* v;
+  int64_t page_stride, token_stride, head_stride;  // elements
+  const int32_t* qo_indptr;   // device [batch+1]
+  const int32_t* kv_indptr;   // device [batch+1]
+  const int32_t* kv_indices;  // device page ids
+  const int32_t* items;       // device [num_items][8]
+  const int32_t* kv_lens;     // device [batch] KV length per request
+  int32_t page_size;
+  int32_t num_qo_heads;
+  int32_t group;              // G <= 128
+  int32_t causal;
+  float scale_log2;           // sm_scale * log2(e)
+  void* o;                    // final output rows [total_qo*Hq][128]
+  float* lse;                 // [total_qo*Hq] or NULL
+  float* part_o;              // [slot][128 rows][128]
+  float* part_lse;            // [slot][128 rows]
+};
+
+struct MergeGroupsArgs {
+  const int32_t* groups;      // device [num_groups][8], or NULL: implicit (single decode)
+  int32_t implicit_nchunks;
+  int32_t rows_per_tile;      // rows per partial slot
+  int32_t num_qo_heads;
+  int32_t group;              // G
+  int32_t prefill;            // row mapping: 0 decode, 1 GQA-packed prefill rows
+  const int32_t* qo_indptr;   // device, prefill mapping only
+  const float* part_o;
+  const float* part_lse;
+  void* o;
+  float* lse;                 // or NULL
+};
+
+// Workgroups of the decode / prefill kernel resident per CU (0 on error).
+int32_t decode_occupancy();
+int32_t prefill_occupancy();
+
+hipError_t launch_decode(const DecodeArgs& a, int32_t storage_dtype, OutKind out,
+                         PageMode mode, int32_t grid, hipStream_t stream);
+
+hipError_t launch_prefill(const PrefillArgs& a, int32_t storage_dtype, OutKind out,
+                          PageMode mode, int32_t grid, hipStream_t stream);
+
+hipError_t launch_merge_groups(const MergeGroupsArgs& a, int32_t storage_dtype, OutKind out,
+                               int32_t num_groups, hipStream_t stream);
+
+// Public merges: v dtype in {F16, BF16, F32}; rows = n * H.
+hipError_t launch_merge2(const void* va, const float* sa, const void* vb, const float* sb,
+                         void* vo, float* so, int64_t rows, int32_t head_dim, int32_t v_dtype,
+                         hipStream_t stream);
+hipError_t launch_merge_n(const void* v, const float* s, int64_t n, int32_t num_states,
+                          int32_t num_heads, int32_t head_dim, int32_t v_dtype, void* vo,
+                          float* so, hipStream_t stream);
+// Cascade's final merge: fp32 states a and b -> storage-dtype o, float lse.
+hipError_t launch_merge2_f32_to(const float* va, const float* sa, const float* vb,
+                                const float* sb, void* vo, float* so, int64_t rows,
+                                int32_t head_dim, int32_t out_dtype, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,211 @@
+// Attention-state merge kernels for gfx950.
+//
+// States of disjoint KV parts (O_k, LSE_k) combine into the state of their
+// union by rescaling with the LSEs: s* = max_k LSE_k, w_k = exp(LSE_k - s*),
+// O = sum w_k O_k / sum w_k, LSE = s* + ln(sum w_k); if every LSE_k is -inf
+// the row saw no key and the result is (0, -inf) (FlashInfer article,
+// sections "Attention states" and "Extreme-negative-logit correction"; docs
+// index "flashinfer.cascade" > "Merge Attention States").
+//
+// Mapping: the merge of a planned split group gives each output row a
+// workgroup whose waves split the chunks; the public merges give each row one
+// wave whose lanes stride over head_dim and read the states in ascending k.
+// Every reduction runs in a fixed order, so a run is reproducible bit for bit.
+// The work is a few MB at most and HBM-bound; fp32 throughout, output rounded
+// once.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace pkv {
+
+namespace {
+
+template <class V>
+__device__ __forceinline__ float load_f(const V* p) {
+  return static_cast<float>(*p);
+}
+
+template <class OUT>
+__device__ __forceinline__ void store_f(OUT* p, float x) {
+  *p = static_cast<OUT>(x);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// Merge of the chunks of one planned split group: blockIdx.x = group,
+// blockIdx.y = row. The 64 lanes of every wave read the chunks' LSEs in
+// parallel (max and sum), the 4 waves split the chunks (k = wave, wave+4, ...)
+// for the weighted sum of outputs, and the four partial sums add up in LDS
+// in a fixed order, so every run gives the same bits.
+template <class OUT>
+__global__ __launch_bounds__(256) void merge_groups_kernel(const MergeGroupsArgs a) {
+  constexpr int D = kHeadDim;
+  __shared__ float s_red[4][D];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int b, tile, g, sb, n;
+  if (a.groups != nullptr) {
+    const int32_t* gr = a.groups + 8 * blockIdx.x;
+    b = gr[0];
+    tile = gr[1];
+    g = gr[2];
+    sb = gr[3];
+    n = gr[4];
+  } else {
+    b = 0;
+    tile = 0;
+    g = blockIdx.x;
+    n = a.implicit_nchunks;
+    sb = g * n;
+  }
+  const int R = a.rows_per_tile;
+  const int r = blockIdx.y;
+  RowMap map{a.num_qo_heads, a.group, a.prefill != 0};
+  const int64_t orow = map.out_row(a.qo_indptr, b, tile, g, r, R);
+  if (orow < 0) return;                       // uniform across the workgroup
+
+  const float* lse = a.part_lse + static_cast<int64_t>(sb) * R + r;   // chunk k at lse[k * R]
+  float M = neg_inf();
+  for (int k = lane; k < n; k += 64) M = fmaxf(M, lse[static_cast<int64_t>(k) * R]);
+  M = wave_max(M);
+  const float Mu = (M == neg_inf()) ? 0.f : M;
+  float L = 0.f;
+  for (int k = lane; k < n; k += 64) L += fast_exp2((lse[static_cast<int64_t>(k) * R] - Mu) * kLog2e);
+  L = wave_sum(L);
+
+  float o0 = 0.f, o1 = 0.f;
+  for (int k = wave; k < n; k += 4) {
+    const int64_t srow = static_cast<int64_t>(sb + k) * R + r;
+    const float w = fast_exp2((a.part_lse[srow] - Mu) * kLog2e);
+    const float2 v = *reinterpret_cast<const float2*>(a.part_o + srow * D + 2 * lane);
+    o0 += w * v.x;
+    o1 += w * v.y;
+  }
+  s_red[wave][2 * lane] = o0;
+  s_red[wave][2 * lane + 1] = o1;
+  __syncthreads();
+  if (tid < D) {
+    const float sum = ((s_red[0][tid] + s_red[1][tid]) + s_red[2][tid]) + s_red[3][tid];
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    store_f(static_cast<OUT*>(a.o) + orow * D + tid, sum * inv);
+  }
+  if (tid == 0 && a.lse != nullptr) a.lse[orow] = L > 0.f ? M + __logf(L) : neg_inf();
+}
+
+// Generic row merge of K states: state k of row `row` is at
+// v + (row_base(row) + k * k_stride) * D (values) and s[s_base(row) + k*s_k_stride].
+// Used for merge_states ([n, K, H, D]) and the two-input forms.
+template <class VIN, class VOUT>
+__global__ __launch_bounds__(256) void merge_rows_kernel(const VIN* va, const float* sa,
+                                                         const VIN* vb, const float* sb,
+                                                         int64_t rows, int32_t H, int32_t K,
+                                                         int32_t D, VOUT* vo, float* so) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  // vb == nullptr: K states interleaved as [n, K, H, D]; else two arrays [rows, D].
+  const int64_t i = row / H, h = row - (row / H) * H;
+  auto v_ptr = [&](int k) -> const VIN* {
+    if (vb != nullptr) return (k == 0 ? va : vb) + row * D;
+    return va + ((i * K + k) * H + h) * D;
+  };
+  auto s_val = [&](int k) -> float {
+    if (vb != nullptr) return k == 0 ? sa[row] : sb[row];
+    return sa[(i * K + k) * H + h];
+  };
+  float M = neg_inf();
+  for (int k = 0; k < K; ++k) M = fmaxf(M, s_val(k));
+  const float Mu = (M == neg_inf()) ? 0.f : M;
+  float L = 0.f;
+  for (int k = 0; k < K; ++k) L += fast_exp2((s_val(k) - Mu) * kLog2e);
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  for (int d = lane; d < D; d += 64) {
+    float acc = 0.f;
+    for (int k = 0; k < K; ++k) {
+      const float w = fast_exp2((s_val(k) - Mu) * kLog2e);
+      acc += w * load_f(v_ptr(k) + d);
+    }
+    store_f(vo + row * D + d, acc * inv);
+  }
+  if (lane == 0 && so != nullptr) so[row] = L > 0.f ? M + __logf(L) : neg_inf();
+}
+
+template <class V>
+hipError_t merge_rows(const void* va, const float* sa, const void* vb, const float* sb,
+                      int64_t rows, int32_t H, int32_t K, int32_t D, void* vo, float* so,
+                      hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t grid = (rows + 3) / 4;
+  hipLaunchKernelGGL((merge_rows_kernel<V, V>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
+                     s, static_cast<const V*>(va), sa, static_cast<const V*>(vb), sb, rows, H, K,
+                     D, static_cast<V*>(vo), so);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_merge_groups(const MergeGroupsArgs& a, int32_t storage_dtype, OutKind out,
+                               int32_t num_groups, hipStream_t stream) {
+  if (num_groups <= 0) return hipSuccess;
+  const dim3 grid(num_groups, a.rows_per_tile);
+  if (out == kOutF32) {
+    hipLaunchKernelGGL(merge_groups_kernel<float>, grid, dim3(256), 0, stream, a);
+  } else if (storage_dtype == 0) {
+    hipLaunchKernelGGL(merge_groups_kernel<_Float16>, grid, dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(merge_groups_kernel<__bf16>, grid, dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_merge2(const void* va, const float* sa, const void* vb, const float* sb,
+                         void* vo, float* so, int64_t rows, int32_t head_dim, int32_t v_dtype,
+                         hipStream_t stream) {
+  switch (v_dtype) {
+    case 0: return merge_rows<_Float16>(va, sa, vb, sb, rows, 1, 2, head_dim, vo, so, stream);
+    case 1: return merge_rows<__bf16>(va, sa, vb, sb, rows, 1, 2, head_dim, vo, so, stream);
+    default: return merge_rows<float>(va, sa, vb, sb, rows, 1, 2, head_dim, vo, so, stream);
+  }
+}
+
+hipError_t launch_merge_n(const void* v, const float* s, int64_t n, int32_t num_states,
+                          int32_t num_heads, int32_t head_dim, int32_t v_dtype, void* vo,
+                          float* so, hipStream_t stream) {
+  const int64_t rows = n * num_heads;
+  switch (v_dtype) {
+    case 0:
+      return merge_rows<_Float16>(v, s, nullptr, nullptr, rows, num_heads, num_states, head_dim,
+                                  vo, so, stream);
+    case 1:
+      return merge_rows<__bf16>(v, s, nullptr, nullptr, rows, num_heads, num_states, head_dim, vo,
+                                so, stream);
+    default:
+      return merge_rows<float>(v, s, nullptr, nullptr, rows, num_heads, num_states, head_dim, vo,
+                               so, stream);
+  }
+}
+
+hipError_t launch_merge2_f32_to(const float* va, const float* sa, const float* vb,
+                                const float* sb, void* vo, float* so, int64_t rows,
+                                int32_t head_dim, int32_t out_dtype, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid(static_cast<uint32_t>((rows + 3) / 4));
+  if (out_dtype == 0) {
+    hipLaunchKernelGGL((merge_rows_kernel<float, _Float16>), grid, dim3(256), 0, stream, va, sa,
+                       vb, sb, rows, 1, 2, head_dim, static_cast<_Float16*>(vo), so);
+  } else {
+    hipLaunchKernelGGL((merge_rows_kernel<float, __bf16>), grid, dim3(256), 0, stream, va, sa, vb,
+                       sb, rows, 1, 2, head_dim, static_cast<__bf16*>(vo), so);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,116 @@
+// Host-side work-chunk planner (see planner.h for the rule's source).
+#include "planner.h"
+
+#include <algorithm>
+#include <limits>
+
+namespace pkv {
+
+namespace {
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct TileExtent {
+  int32_t b, tile;
+  int64_t kv_end, pages;
+};
+
+struct Keyed {
+  int64_t tokens;
+  int32_t b, tile, g, j;
+  PlanItem item;
+};
+
+}  // namespace
+
+bool build_plan(const PlanInput& in, HostPlan* out, std::string* err) {
+  const int64_t P = in.page_size, G = in.group_size, R = in.rows_per_tile;
+  out->items.clear();
+  out->groups.clear();
+
+  // Per (request, tile): the KV extent the tile's rows may see.
+  std::vector<TileExtent> tiles;
+  int64_t page_sum = 0;
+  for (int32_t b = 0; b < in.batch; ++b) {
+    const int64_t Q = in.qo_lens[b], L = in.kv_lens[b];
+    const int64_t rows = Q * G;
+    const int64_t n_tiles = ceil_div(rows, R);
+    for (int64_t t = 0; t < n_tiles; ++t) {
+      int64_t extent = L;
+      if (in.causal) {
+        const int64_t last_row = std::min((t + 1) * R, rows) - 1;
+        const int64_t q_last = last_row / G;
+        extent = std::clamp<int64_t>(L - Q + q_last + 1, 0, L);
+      }
+      const int64_t pages = ceil_div(extent, P);
+      tiles.push_back({b, static_cast<int32_t>(t), extent, pages});
+      page_sum += pages;
+    }
+  }
+
+  // Chunk size: enough chunks to cover num_cus * wg_per_cu slots, never
+  // shorter than min_chunk_tokens (in whole pages).
+  const int64_t work = static_cast<int64_t>(in.num_kv_heads) * page_sum;
+  const int64_t target = static_cast<int64_t>(in.num_cus) * in.wg_per_cu;
+  const int64_t c_min = std::max<int64_t>(1, ceil_div(in.min_chunk_tokens, P));
+  const int64_t c = std::max<int64_t>(c_min, ceil_div(work, target));
+  if (c > std::numeric_limits<int32_t>::max()) {
+    *err = "chunk size overflows int32";
+    return false;
+  }
+
+  std::vector<Keyed> keyed;
+  int64_t slot = 0;
+  for (const TileExtent& te : tiles) {
+    const int64_t n_chunks = std::max<int64_t>(1, ceil_div(te.pages, c));
+    for (int32_t g = 0; g < in.num_kv_heads; ++g) {
+      int64_t slot_begin = -1;
+      if (n_chunks > 1) {
+        slot_begin = slot;
+        MergeGroup mg{};
+        mg.b = te.b;
+        mg.tile = te.tile;
+        mg.g = g;
+        mg.slot_begin = static_cast<int32_t>(slot_begin);
+        mg.num_chunks = static_cast<int32_t>(n_chunks);
+        out->groups.push_back(mg);
+        slot += n_chunks;
+      }
+      for (int64_t j = 0; j < n_chunks; ++j) {
+        PlanItem it{};
+        it.b = te.b;
+        it.g = g;
+        it.tile = te.tile;
+        it.page_begin = static_cast<int32_t>(j * c);
+        it.page_end = static_cast<int32_t>(std::min((j + 1) * c, te.pages));
+        const int64_t k0 = std::min(j * c * P, te.kv_end);
+        const int64_t k1 = std::min((j + 1) * c * P, te.kv_end);
+        it.kv_begin = static_cast<int32_t>(k0);
+        it.kv_end = static_cast<int32_t>(k1);
+        it.slot = n_chunks > 1 ? static_cast<int32_t>(slot_begin + j) : -1;
+        keyed.push_back({k1 - k0, te.b, te.tile, g, static_cast<int32_t>(j), it});
+      }
+    }
+  }
+  if (slot > std::numeric_limits<int32_t>::max() ||
+      keyed.size() > static_cast<size_t>(std::numeric_limits<int32_t>::max())) {
+    *err = "item or slot count overflows int32";
+    return false;
+  }
+
+  // Longest first; ties in (b, tile, g, j) order.
+  std::sort(keyed.begin(), keyed.end(), [](const Keyed& x, const Keyed& y) {
+    if (x.tokens != y.tokens) return x.tokens > y.tokens;
+    if (x.b != y.b) return x.b < y.b;
+    if (x.tile != y.tile) return x.tile < y.tile;
+    if (x.g != y.g) return x.g < y.g;
+    return x.j < y.j;
+  });
+  out->items.reserve(keyed.size());
+  for (const Keyed& k : keyed) out->items.push_back(k.item);
+  out->chunk_pages = static_cast<int32_t>(c);
+  out->num_slots = static_cast<int32_t>(slot);
+  return true;
+}
+
+}  // namespace pkv

@@ -1,0 +1,142 @@
+"""Helpers shared by the GPU parity tests: upload a workload, run it through the
+C ABI (via the binding), run the oracle on the same inputs, compare."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+
+# fp16: O <= 2e-3, LSE <= 1e-3; bf16: O <= 1e-2, LSE <= 2e-3 (max abs error)
+TOL = {"f16": (2e-3, 1e-3), "bf16": (1e-2, 2e-3)}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(bits: np.ndarray, dtype: str) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.float16 if dtype == "f16" else torch.bfloat16).to("cuda")
+
+
+def dev_i32(a) -> torch.Tensor:
+    a = np.asarray(a, dtype=np.int32)
+    if a.size == 0:
+        a = np.zeros(1, dtype=np.int32)      # a valid pointer for an empty table
+    return torch.from_numpy(a).to("cuda")
+
+
+class Uploaded:
+    """Device copies of a workload's tensors."""
+
+    def __init__(self, w):
+        self.w = w
+        self.q = dev(w.q, w.dtype)
+        if w.kv is not None:
+            self.k = dev(w.kv.k_cache, w.dtype)
+            self.v = dev(w.kv.v_cache, w.dtype)
+            self.kv_indptr = dev_i32(w.kv.kv_indptr)
+            self.kv_indices = dev_i32(w.kv.kv_indices)
+        else:
+            self.k = dev(w.k, w.dtype)
+            self.v = dev(w.v, w.dtype)
+        if w.qo_indptr is not None:
+            self.qo_indptr = dev_i32(w.qo_indptr)
+        if w.prefix_indices is not None:
+            self.prefix_indices = dev_i32(w.prefix_indices)
+
+
+def run_gpu(pkv, up: Uploaded, ws, sched=None):
+    """Run the workload's operation through the C ABI; returns (o, lse) on the host."""
+    w = up.w
+    if w.kind == "single_decode":
+        o, lse = pkv.pkv_single_decode(up.q, up.k, up.v, w.sm_scale, sched=sched)
+    elif w.kind == "decode":
+        plan = pkv.pkv_decode_plan(w.kv.kv_indptr, w.kv.last_page_len, w.num_qo_heads,
+                                   w.num_kv_heads, w.head_dim, w.kv.page_size, up.q.dtype, ws,
+                                   sched=sched)
+        o, lse = pkv.pkv_decode_run(plan, up.q, up.k, up.v, up.kv_indptr, up.kv_indices,
+                                    w.sm_scale)
+    elif w.kind == "prefill":
+        plan = pkv.pkv_prefill_plan(w.qo_indptr, w.kv.kv_indptr, w.kv.last_page_len,
+                                    w.num_qo_heads, w.num_kv_heads, w.head_dim, w.kv.page_size,
+                                    up.q.dtype, w.causal, ws, sched=sched)
+        o, lse = pkv.pkv_prefill_run(plan, up.q, up.k, up.v, up.qo_indptr, up.kv_indptr,
+                                     up.kv_indices, w.sm_scale)
+    elif w.kind == "cascade":
+        plan = pkv.pkv_cascade_plan(len(w.prefix_indices), w.prefix_last_page_len,
+                                    w.kv.kv_indptr, w.kv.last_page_len, w.num_qo_heads,
+                                    w.num_kv_heads, w.head_dim, w.kv.page_size, up.q.dtype, ws,
+                                    sched=sched)
+        o, lse = pkv.pkv_cascade_run(plan, up.q, up.k, up.v, up.prefix_indices, up.kv_indptr,
+                                     up.kv_indices, w.sm_scale)
+    else:
+        raise ValueError(w.kind)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def run_oracle(w, requests=None):
+    """Oracle state for the workload (optionally only some requests / rows)."""
+    if w.kind == "single_decode":
+        return oracle.single_decode(w.q, w.k, w.v, w.dtype, w.sm_scale)
+    kv = w.kv
+    if w.kind == "decode":
+        return oracle.batch_decode(w.q, kv.k_cache, kv.v_cache, kv.kv_indptr, kv.kv_indices,
+                                   kv.last_page_len, w.dtype, w.sm_scale, requests=requests)
+    if w.kind == "prefill":
+        return oracle.batch_prefill(w.q, kv.k_cache, kv.v_cache, w.qo_indptr, kv.kv_indptr,
+                                    kv.kv_indices, kv.last_page_len, w.dtype, w.sm_scale,
+                                    w.causal, requests=requests)
+    if w.kind == "cascade":
+        return oracle.cascade_decode(w.q, kv.k_cache, kv.v_cache, w.prefix_indices,
+                                     w.prefix_last_page_len, kv.kv_indptr, kv.kv_indices,
+                                     kv.last_page_len, w.dtype, w.sm_scale, requests=requests)
+    raise ValueError(w.kind)
+
+
+def rows_of(w, requests):
+    """Output row indices (first axis of o / lse) that belong to `requests`."""
+    if requests is None:
+        return slice(None)
+    if w.kind == "prefill":
+        return np.concatenate([np.arange(w.qo_indptr[b], w.qo_indptr[b + 1]) for b in requests])
+    return np.asarray(requests)
+
+
+def compare(w, o, lse, O, LSE, rows=slice(None), tol=None, label=""):
+    """Max-abs comparison at the dtype's tolerance; -inf LSE must match exactly."""
+    to, tl = TOL[w.dtype] if tol is None else tol
+    o, lse, O, LSE = o[rows], lse[rows], O[rows], LSE[rows]
+    assert not np.isnan(o).any(), f"{label}: NaN in output"
+    inf_ref = np.isneginf(LSE)
+    assert np.array_equal(np.isneginf(lse), inf_ref), f"{label}: -inf LSE rows differ"
+    assert (o[inf_ref] == 0).all(), f"{label}: fully masked rows must be zero"
+    err_o = float(np.max(np.abs(o - O))) if o.size else 0.0
+    fin = ~inf_ref
+    err_l = float(np.max(np.abs(lse[fin] - LSE[fin]))) if fin.any() else 0.0
+    say(f"  {label}: max|dO| = {err_o:.3e} (tol {to}), max|dLSE| = {err_l:.3e} (tol {tl}), "
+        f"max|O| = {float(np.max(np.abs(O))) if O.size else 0:.3f}")
+    assert err_o <= to, f"{label}: output error {err_o} > {to}"
+    assert err_l <= tl, f"{label}: LSE error {err_l} > {tl}"
+    return err_o, err_l
+
+
+def prefill_with_lengths(seed, qo_lens, kv_lens, Hq, Hkv, P, dtype="bf16", D=128, causal=True):
+    """Prefill workload with explicit query and KV lengths (KV may be shorter than Q)."""
+    import math
+    from paged_kv_cache_173_amd import workloads as wl
+    qo_lens = np.asarray(qo_lens)
+    rng = np.random.default_rng(seed)
+    kv, q, _ = wl.make_paged(rng, np.asarray(kv_lens), P, Hkv, D, dtype,
+                             (int(qo_lens.sum()), Hq, D))
+    wl.canary_tails(kv, dtype)
+    qo_indptr = np.zeros(len(qo_lens) + 1, dtype=np.int32)
+    qo_indptr[1:] = np.cumsum(qo_lens)
+    return wl.Workload("prefill", dtype, Hq, Hkv, D, 1 / math.sqrt(D), q, kv=kv,
+                       qo_indptr=qo_indptr, causal=causal, meta={"qo_lens": qo_lens})
