@@ -8,9 +8,10 @@ made once per workload before timing and reused, as the plan/run split
 intends, and its host time is reported as plan_us.
 
 Timing: W warm-up steps, then K timed steps. Before every step a 512 MiB
-buffer is overwritten (outside the timed events) so the 256 MB Infinity Cache
-holds no KV; each step is bracketed by HIP events on the stream the kernels
-run on. value = algorithmic bytes / mean step time.
+buffer is read (outside the timed events) so the 256 MB Infinity Cache holds
+no KV and no dirty lines that would be written back during the step; each
+step is bracketed by HIP events on the stream the kernels run on.
+value = algorithmic bytes / mean step time.
 
 `--workload` selects another workload (single, decode, prefill, cascade,
 long); `--all` adds every workload's figures under "workloads" in the line.
@@ -36,6 +37,42 @@ sys.path.insert(0, ROOT)
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+# Sources the decode kernel is compiled from; a traffic figure in profiles/ is
+# used only while their hash matches the one recorded next to it.
+DECODE_SOURCES = ["paged_kv_cache_173_amd/csrc/decode.hip",
+                  "paged_kv_cache_173_amd/csrc/device_common.h",
+                  "paged_kv_cache_173_amd/csrc/kernels.h"]
+TRAFFIC_PROFILE = "profiles/decode_kernel_batch64_fp16_hbm_traffic.md"
+
+
+def decode_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic():
+    """HBM bytes per decode-kernel launch measured by rocprofv3 counters, or None
+    when the kernel's sources changed since the counters were taken."""
+    path = os.path.join(ROOT, TRAFFIC_PROFILE)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip().strip("`- ")] = v.strip().strip("`")
+    if fields.get("source_sha256") != decode_source_hash():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 # ----------------------------------------------------------------------------
@@ -129,17 +166,21 @@ class Runner:
                                              w.num_kv_heads, w.head_dim, w.kv.page_size, dt,
                                              self.ws)
 
-    def step(self):
+    def step(self, attention_done=None):
+        """One run; `attention_done` (decode / prefill) is recorded after the attention
+        kernel, before the merge of split chunks."""
         p, w = self.pkv, self.w
         if w.kind == "single_decode":
             p.pkv_single_decode(self.q, self.k, self.v, w.sm_scale, float_ws=self.fws, o=self.o,
                                 lse=self.lse)
         elif w.kind == "decode":
-            p.pkv_decode_run(self.plan, self.q, self.k, self.v, self.kv_indptr, self.kv_indices,
-                             w.sm_scale, o=self.o, lse=self.lse)
+            p.pkv_decode_run_timed(self.plan, self.q, self.k, self.v, self.kv_indptr,
+                                   self.kv_indices, w.sm_scale, attention_done, o=self.o,
+                                   lse=self.lse)
         elif w.kind == "prefill":
-            p.pkv_prefill_run(self.plan, self.q, self.k, self.v, self.qo_indptr, self.kv_indptr,
-                              self.kv_indices, w.sm_scale, o=self.o, lse=self.lse)
+            p.pkv_prefill_run_timed(self.plan, self.q, self.k, self.v, self.qo_indptr,
+                                    self.kv_indptr, self.kv_indices, w.sm_scale, attention_done,
+                                    o=self.o, lse=self.lse)
         else:
             p.pkv_cascade_run(self.plan, self.q, self.k, self.v, self.prefix, self.kv_indptr,
                               self.kv_indices, w.sm_scale, o=self.o, lse=self.lse)
@@ -170,24 +211,34 @@ class Runner:
 
 
 def time_steps(torch, runner, steps, warmup, flush):
+    """Returns (mean step ms, median step ms, mean attention-kernel ms or None, wall s)."""
+    def evict():
+        return flush.view(torch.int64).sum()
+
+    timed_kernel = runner.w.kind in ("decode", "prefill")
     for _ in range(warmup):
-        flush.fill_(1)
-        runner.step()
+        evict()
+        runner.step(torch.cuda.Event(enable_timing=True) if timed_kernel else None)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for ev in mids:                          # create the events before the timed loop
+        ev.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        flush.fill_(i & 0xFF)                # evicts the Infinity Cache, outside the events
+        evict()                              # evicts the Infinity Cache, outside the events
         starts[i].record(stream)
-        runner.step()
+        runner.step(mids[i] if timed_kernel else None)
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return float(np.mean(ms)), float(np.median(ms)), wall
+    kern = [s.elapsed_time(m) for s, m in zip(starts, mids)] if timed_kernel else None
+    return (float(np.mean(ms)), float(np.median(ms)),
+            float(np.mean(kern)) if kern else None, wall)
 
 
 def cpu_baseline(w, budget_s=15.0):
@@ -238,7 +289,7 @@ def main():
     from paged_kv_cache_173_amd import workloads as wl
 
     log(f"[bench] generating workload {args.workload}")
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
     names = [args.workload] + ([n for n in ("single", "decode", "prefill", "cascade", "long")
                                 if n != args.workload] if args.all else [])
     results = {}
@@ -247,16 +298,22 @@ def main():
         w = wl.FULL[WORKLOADS[name]]()
         r = Runner(name, w, pkv, torch)
         log(f"[bench] {name}: planned in {r.plan_us:.0f} us; timing {args.steps} steps")
-        mean_ms, med_ms, wall = time_steps(torch, r, args.steps, args.warmup, flush)
+        mean_ms, med_ms, kern_ms, wall = time_steps(torch, r, args.steps, args.warmup, flush)
         nbytes, flops, tokens = r.work()
-        res = {"ms_per_step": mean_ms, "median_ms": med_ms, "plan_us": r.plan_us,
+        res = {"ms_per_step": mean_ms, "median_ms": med_ms, "attention_kernel_ms": kern_ms,
+               "plan_us": r.plan_us,
                "GBps": nbytes / (mean_ms * 1e-3) / 1e9, "TFLOPs": flops / (mean_ms * 1e-3) / 1e12,
                "tokens_per_s": tokens / (mean_ms * 1e-3), "bytes": nbytes, "flops": flops,
                "wall_s": wall}
         res["hbm_frac"] = res["GBps"] / HBM_PEAK_GBS
         res["mfma_frac"] = res["TFLOPs"] / MFMA_PEAK_TFLOPS
+        kern_ms = kern_ms if kern_ms else mean_ms
+        res["kernel_GBps"] = nbytes / (kern_ms * 1e-3) / 1e9
+        res["kernel_TFLOPs"] = flops / (kern_ms * 1e-3) / 1e12
         log(f"[bench] {name}: {mean_ms * 1e3:.1f} us/step, {res['GBps']:.0f} GB/s "
-            f"({100 * res['hbm_frac']:.1f}% HBM), {res['TFLOPs']:.1f} TFLOP/s")
+            f"({100 * res['hbm_frac']:.1f}% HBM), {res['TFLOPs']:.1f} TFLOP/s; attention kernel "
+            f"{kern_ms * 1e3:.1f} us: {res['kernel_GBps']:.0f} GB/s, "
+            f"{res['kernel_TFLOPs']:.1f} TFLOP/s")
         results[name] = res
         if headline is None:
             headline = (name, w, r, res)
@@ -285,13 +342,16 @@ def main():
             "long": "long-context split-KV decode, 4 x 131072 tokens, 64/8 heads, P=64, bf16",
         }[name], "head_dim": 128, "tokens_per_step": r.work()[2],
             "tokens_per_s": res["tokens_per_s"], "plan_us": res["plan_us"]},
+        # the dominant kernel (the attention kernel, timed alone with events)
         "roofline": {
             "bound": "mfma" if prefill_like else "hbm",
-            "achieved": res["TFLOPs"] if prefill_like else res["GBps"],
+            "achieved": res["kernel_TFLOPs"] if prefill_like else res["kernel_GBps"],
             "peak": MFMA_PEAK_TFLOPS if prefill_like else HBM_PEAK_GBS,
             "unit": "TFLOP/s" if prefill_like else "GB/s",
-            "frac": res["mfma_frac"] if prefill_like else res["hbm_frac"],
-            "traffic": None,
+            "frac": (res["kernel_TFLOPs"] / MFMA_PEAK_TFLOPS) if prefill_like
+            else (res["kernel_GBps"] / HBM_PEAK_GBS),
+            "traffic": profiled_traffic() if name == "decode" else None,
+            "kernel_us": (res["attention_kernel_ms"] or res["ms_per_step"]) * 1e3,
         },
     }
     if len(results) > 1:

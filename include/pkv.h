@@ -212,6 +212,15 @@ pkv_status pkv_decode_run(const pkv_plan_info* plan, const void* q, const pkv_pa
                           const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
                           float sm_scale, void* o, float* lse, void* stream);
 
+/* As pkv_decode_run, and records `attention_done` (a hipEvent_t passed as
+ * void*, created by the caller; NULL = none) on `stream` right after the
+ * attention kernel and before the merge of split chunks, so a caller can time
+ * the two kernels separately. */
+pkv_status pkv_decode_run_timed(const pkv_plan_info* plan, const void* q, const pkv_paged_kv* kv,
+                                const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
+                                float sm_scale, void* o, float* lse, void* stream,
+                                void* attention_done);
+
 /* ---------------------------------------------------------------------------
  * Batch paged prefill / append: Q_b = qo_indptr[b+1]-qo_indptr[b] query
  * tokens per request, the last Q_b of its L_b keys. causal=1 applies the
@@ -232,6 +241,13 @@ pkv_status pkv_prefill_run(const pkv_plan_info* plan, const void* q, const pkv_p
                            const int32_t* qo_indptr_d, const int32_t* kv_indptr_d,
                            const int32_t* kv_indices_d, float sm_scale, void* o, float* lse,
                            void* stream);
+
+/* As pkv_prefill_run, recording `attention_done` after the attention kernel
+ * (see pkv_decode_run_timed). */
+pkv_status pkv_prefill_run_timed(const pkv_plan_info* plan, const void* q, const pkv_paged_kv* kv,
+                                 const int32_t* qo_indptr_d, const int32_t* kv_indptr_d,
+                                 const int32_t* kv_indices_d, float sm_scale, void* o, float* lse,
+                                 void* stream, void* attention_done);
 
 /* ---------------------------------------------------------------------------
  * Single-request decode over a contiguous NHD cache k, v [kv_len, Hkv, 128]

@@ -262,7 +262,8 @@ const int32_t* i_at(const void* base, int64_t off) {
 pkv_status run_decode_part(const pkv_plan_info* plan, const pkv_plan_part& part, const void* q,
                            const pkv_paged_kv* kv, const int32_t* kv_indptr_d,
                            const int32_t* kv_indices_d, float sm_scale, void* o, float* lse,
-                           pkv::OutKind out_kind, hipStream_t stream) {
+                           pkv::OutKind out_kind, hipStream_t stream,
+                           hipEvent_t attention_done = nullptr) {
   const int32_t G = plan->num_qo_heads / plan->num_kv_heads;
   pkv::DecodeArgs a{};
   a.q = q;
@@ -285,6 +286,8 @@ pkv_status run_decode_part(const pkv_plan_info* plan, const pkv_plan_part& part,
   hipError_t e = pkv::launch_decode(a, plan->dtype, out_kind, page_mode(plan->page_size),
                                     part.num_items, stream);
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+  if (attention_done != nullptr && (e = hipEventRecord(attention_done, stream)) != hipSuccess)
+    return hip_fail(e, "hipEventRecord");
   if (part.num_groups > 0) {
     pkv::MergeGroupsArgs m{};
     m.groups = i_at(plan->int_ws, part.groups_off);
@@ -306,7 +309,8 @@ pkv_status run_prefill_part(const pkv_plan_info* plan, const pkv_plan_part& part
                             const pkv_paged_kv* kv, const int32_t* qo_indptr_d,
                             const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
                             float sm_scale, void* o, float* lse, int32_t num_qo_heads,
-                            pkv::OutKind out_kind, hipStream_t stream) {
+                            pkv::OutKind out_kind, hipStream_t stream,
+                            hipEvent_t attention_done = nullptr) {
   const int32_t G = num_qo_heads / plan->num_kv_heads;
   pkv::PrefillArgs a{};
   a.q = q;
@@ -332,6 +336,8 @@ pkv_status run_prefill_part(const pkv_plan_info* plan, const pkv_plan_part& part
   hipError_t e = pkv::launch_prefill(a, plan->dtype, out_kind, page_mode(plan->page_size),
                                      part.num_items, stream);
   if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
+  if (attention_done != nullptr && (e = hipEventRecord(attention_done, stream)) != hipSuccess)
+    return hip_fail(e, "hipEventRecord");
   if (part.num_groups > 0) {
     pkv::MergeGroupsArgs m{};
     m.groups = i_at(plan->int_ws, part.groups_off);
@@ -472,6 +478,14 @@ pkv_status pkv_decode_plan(const int32_t* kv_indptr_h, const int32_t* last_page_
 pkv_status pkv_decode_run(const pkv_plan_info* plan, const void* q, const pkv_paged_kv* kv,
                           const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
                           float sm_scale, void* o, float* lse, void* stream) {
+  return pkv_decode_run_timed(plan, q, kv, kv_indptr_d, kv_indices_d, sm_scale, o, lse, stream,
+                              nullptr);
+}
+
+pkv_status pkv_decode_run_timed(const pkv_plan_info* plan, const void* q, const pkv_paged_kv* kv,
+                                const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
+                                float sm_scale, void* o, float* lse, void* stream,
+                                void* attention_done) {
   pkv_status st;
   if ((st = check_plan(plan, PKV_KIND_DECODE))) return st;
   if ((st = check_kv(kv, plan))) return st;
@@ -480,7 +494,8 @@ pkv_status pkv_decode_run(const pkv_plan_info* plan, const void* q, const pkv_pa
     return fail(PKV_ERR_INVALID_ARG, "q, o, kv_indptr or kv_indices is NULL");
   if (!aligned16(q) || !aligned16(o)) return fail(PKV_ERR_INVALID_ARG, "q / o must be 16-byte aligned");
   if ((st = run_decode_part(plan, plan->part[0], q, kv, kv_indptr_d, kv_indices_d, sm_scale, o,
-                            lse, pkv::kOutStorage, static_cast<hipStream_t>(stream))))
+                            lse, pkv::kOutStorage, static_cast<hipStream_t>(stream),
+                            static_cast<hipEvent_t>(attention_done))))
     return st;
   return ok();
 }
@@ -531,6 +546,14 @@ pkv_status pkv_prefill_run(const pkv_plan_info* plan, const void* q, const pkv_p
                            const int32_t* qo_indptr_d, const int32_t* kv_indptr_d,
                            const int32_t* kv_indices_d, float sm_scale, void* o, float* lse,
                            void* stream) {
+  return pkv_prefill_run_timed(plan, q, kv, qo_indptr_d, kv_indptr_d, kv_indices_d, sm_scale, o,
+                               lse, stream, nullptr);
+}
+
+pkv_status pkv_prefill_run_timed(const pkv_plan_info* plan, const void* q, const pkv_paged_kv* kv,
+                                 const int32_t* qo_indptr_d, const int32_t* kv_indptr_d,
+                                 const int32_t* kv_indices_d, float sm_scale, void* o, float* lse,
+                                 void* stream, void* attention_done) {
   pkv_status st;
   if ((st = check_plan(plan, PKV_KIND_PREFILL))) return st;
   if ((st = check_kv(kv, plan))) return st;
@@ -540,7 +563,8 @@ pkv_status pkv_prefill_run(const pkv_plan_info* plan, const void* q, const pkv_p
   if (!aligned16(q) || !aligned16(o)) return fail(PKV_ERR_INVALID_ARG, "q / o must be 16-byte aligned");
   if ((st = run_prefill_part(plan, plan->part[0], q, kv, qo_indptr_d, kv_indptr_d, kv_indices_d,
                              sm_scale, o, lse, plan->num_qo_heads, pkv::kOutStorage,
-                             static_cast<hipStream_t>(stream))))
+                             static_cast<hipStream_t>(stream),
+                             static_cast<hipEvent_t>(attention_done))))
     return st;
   return ok();
 }

@@ -24,8 +24,15 @@
 //     cross-lane traffic; every lane accumulates head l % 16, so the online
 //     softmax rescale is lane-local.
 //   * Row max across the 4 token rows of a block: v_permlane16/32_swap.
-//   * The next block's K/V loads are issued before the current block is
-//     computed (register double buffering).
+//   * Loads: one scalar buffer descriptor per 16-token block (page base,
+//     range = the block's valid rows, so tail tokens read as zero) and
+//     per-lane offsets fixed for the whole item; non-temporal, because the KV
+//     cache is streamed once per call and must not evict reused data.
+//   * Two register sets: block k+8's K is issued into block k's K registers
+//     as soon as the scores have read them, its V after the PV product, so
+//     about two blocks per wave are in flight; page ids are read one step
+//     ahead. The loop has no branch around a load, so each wait covers only
+//     the block about to be used.
 //   * -inf is a real IEEE -inf; exp2 of (-inf) - (-inf) is avoided by
 //     subtracting 0 when the running max is still -inf. An empty item yields
 //     O = 0, LSE = -inf.
@@ -38,6 +45,8 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kBlock = 16;  // tokens per wave iteration
+// K/V pages are read once per call: stream them past the caches.
+constexpr int kCachePolicy = kCacheStream;
 
 template <class T, class OUT, int MODE>
 __global__ __launch_bounds__(256, 3) void decode_kernel(const DecodeArgs a) {
@@ -120,7 +129,7 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(const DecodeArgs a) {
     if (MODE != kPagedGeneric) {
       const auto rk = make_rsrc(kbase + base, nbytes(blk));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) kr[j] = buffer_load_16B(rk, koff + 32 * j * sizeof(elem));
+      for (int j = 0; j < 4; ++j) kr[j] = buffer_load_16B<kCachePolicy>(rk, koff + 32 * j * sizeof(elem));
     } else if (blk < nblk_total) {
       const int tb = t0 + kBlock * blk;
       const elem* kp = kbase + token_off(min(tb + hl, last)) + 8 * grp;
@@ -132,7 +141,7 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(const DecodeArgs a) {
     if (MODE != kPagedGeneric) {
       const auto rv = make_rsrc(vbase + base, nbytes(blk));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vr[i] = buffer_load_16B(rv, voff[i]);
+      for (int i = 0; i < 4; ++i) vr[i] = buffer_load_16B<kCachePolicy>(rv, voff[i]);
     } else if (blk < nblk_total) {
       const int tb = t0 + kBlock * blk;
 #pragma unroll

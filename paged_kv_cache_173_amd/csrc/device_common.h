@@ -42,8 +42,14 @@ __device__ __forceinline__ u32x4 load_16B_stream(const void* p) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, num_bytes, 0x00020000);
 }
+// Cache policy of a buffer load (gfx950 encoding of the instruction's sc0 /
+// nt / sc1 bits): kStream marks data read once (non-temporal), so a streamed
+// KV cache does not displace reused data in the L2 and the Infinity Cache.
+constexpr int kCacheDefault = 0;
+constexpr int kCacheStream = 2;
+template <int POLICY = kCacheDefault>
 __device__ __forceinline__ u32x4 buffer_load_16B(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, POLICY));
 }
 
 // ---------------------------------------------------------------------------

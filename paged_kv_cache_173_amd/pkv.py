@@ -93,6 +93,12 @@ _lib_decode_plan = _sig("pkv_decode_plan", _I32,
 _lib_decode_run = _sig("pkv_decode_run", _I32,
                        [ctypes.POINTER(pkv_plan_info), _P, ctypes.POINTER(pkv_paged_kv), _P, _P,
                         _F32, _P, _P, _P])
+_lib_decode_run_timed = _sig("pkv_decode_run_timed", _I32,
+                             [ctypes.POINTER(pkv_plan_info), _P, ctypes.POINTER(pkv_paged_kv), _P,
+                              _P, _F32, _P, _P, _P, _P])
+_lib_prefill_run_timed = _sig("pkv_prefill_run_timed", _I32,
+                              [ctypes.POINTER(pkv_plan_info), _P, ctypes.POINTER(pkv_paged_kv), _P,
+                               _P, _P, _F32, _P, _P, _P, _P])
 _lib_prefill_plan = _sig("pkv_prefill_plan", _I32,
                          [_I32P, _I32P, _I32P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                           ctypes.POINTER(pkv_sched), _P, _SZ, _P, _SZ, _P, _SZ, _P,
@@ -161,6 +167,16 @@ def _stream(stream) -> int | None:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _event(ev) -> int | None:
+    """The hipEvent_t handle of a torch.cuda.Event (created on first use)."""
+    if ev is None:
+        return None
+    if getattr(ev, "cuda_event", 0) == 0:
+        ev.record()            # forces creation of the underlying event
+        torch.cuda.synchronize()
+    return ev.cuda_event
 
 
 def _device_tensor(t: torch.Tensor, name: str) -> torch.Tensor:
@@ -303,6 +319,21 @@ def pkv_decode_run(plan: pkv_plan_info, q, k_cache, v_cache, kv_indptr_d, kv_ind
     return o, lse
 
 
+def pkv_decode_run_timed(plan: pkv_plan_info, q, k_cache, v_cache, kv_indptr_d, kv_indices_d,
+                         sm_scale: float, attention_done, o=None, lse=None, stream=None):
+    """pkv_decode_run that records the torch.cuda.Event `attention_done` after the
+    attention kernel (before the merge)."""
+    kv = paged_kv(k_cache, v_cache)
+    q = q.contiguous()
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(_lib_decode_run_timed(ctypes.byref(plan), q.data_ptr(), ctypes.byref(kv),
+                                 kv_indptr_d.data_ptr(), kv_indices_d.data_ptr(), float(sm_scale),
+                                 o.data_ptr(), _ptr(lse), _stream(stream),
+                                 _event(attention_done)), "pkv_decode_run_timed")
+    return o, lse
+
+
 def pkv_prefill_plan(qo_indptr, kv_indptr, last_page_len, num_qo_heads, num_kv_heads, head_dim,
                      page_size, dtype, causal, workspace: Workspace, sched=None,
                      stream=None) -> pkv_plan_info:
@@ -328,6 +359,22 @@ def pkv_prefill_run(plan: pkv_plan_info, q, k_cache, v_cache, qo_indptr_d, kv_in
                             qo_indptr_d.data_ptr(), kv_indptr_d.data_ptr(),
                             kv_indices_d.data_ptr(), float(sm_scale), o.data_ptr(), _ptr(lse),
                             _stream(stream)), "pkv_prefill_run")
+    return o, lse
+
+
+def pkv_prefill_run_timed(plan: pkv_plan_info, q, k_cache, v_cache, qo_indptr_d, kv_indptr_d,
+                          kv_indices_d, sm_scale: float, attention_done, o=None, lse=None,
+                          stream=None):
+    """pkv_prefill_run that records `attention_done` after the attention kernel."""
+    kv = paged_kv(k_cache, v_cache)
+    q = q.contiguous()
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(_lib_prefill_run_timed(ctypes.byref(plan), q.data_ptr(), ctypes.byref(kv),
+                                  qo_indptr_d.data_ptr(), kv_indptr_d.data_ptr(),
+                                  kv_indices_d.data_ptr(), float(sm_scale), o.data_ptr(),
+                                  _ptr(lse), _stream(stream), _event(attention_done)),
+           "pkv_prefill_run_timed")
     return o, lse
 
 
