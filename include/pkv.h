@@ -40,6 +40,7 @@
  *   - GQA: query head h reads KV head h / G, G = num_qo_heads / num_kv_heads.
  *   - A row that sees no key (empty request, fully masked row) yields O = 0
  *     and LSE = -inf; -inf is never replaced by a finite sentinel.
+ *   - sm_scale (the factor on q.k) must be finite and positive.
  *   - Errors: every entry point returns a pkv_status; on failure nothing is
  *     launched and pkv_last_error() returns a thread-local message.
  *

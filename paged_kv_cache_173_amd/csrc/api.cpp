@@ -135,6 +135,12 @@ pkv_status check_kv(const pkv_paged_kv* kv, const pkv_plan_info* plan) {
   return PKV_OK;
 }
 
+pkv_status check_scale(float sm_scale) {
+  if (!(sm_scale > 0.f) || sm_scale > 3.0e38f)
+    return fail(PKV_ERR_INVALID_ARG, "sm_scale must be finite and positive");
+  return PKV_OK;
+}
+
 pkv_status check_plan(const pkv_plan_info* plan, pkv_kind kind) {
   if (plan == nullptr) return fail(PKV_ERR_INVALID_ARG, "plan is NULL");
   if (plan->magic != kPlanMagic || plan->abi_version != PKV_ABI_VERSION)
@@ -487,6 +493,7 @@ pkv_status pkv_decode_run_timed(const pkv_plan_info* plan, const void* q, const 
                                 float sm_scale, void* o, float* lse, void* stream,
                                 void* attention_done) {
   pkv_status st;
+  if ((st = check_scale(sm_scale))) return st;
   if ((st = check_plan(plan, PKV_KIND_DECODE))) return st;
   if ((st = check_kv(kv, plan))) return st;
   if (plan->batch > 0 && (q == nullptr || o == nullptr || kv_indptr_d == nullptr ||
@@ -555,6 +562,7 @@ pkv_status pkv_prefill_run_timed(const pkv_plan_info* plan, const void* q, const
                                  const int32_t* kv_indices_d, float sm_scale, void* o, float* lse,
                                  void* stream, void* attention_done) {
   pkv_status st;
+  if ((st = check_scale(sm_scale))) return st;
   if ((st = check_plan(plan, PKV_KIND_PREFILL))) return st;
   if ((st = check_kv(kv, plan))) return st;
   if (plan->total_qo > 0 && (q == nullptr || o == nullptr || qo_indptr_d == nullptr ||
@@ -575,6 +583,7 @@ pkv_status pkv_single_decode(const void* q, const void* k, const void* v, int32_
                              void* float_ws, size_t float_ws_bytes, int64_t* float_ws_required,
                              void* o, float* lse, void* stream) {
   pkv_status st;
+  if ((st = check_scale(sm_scale))) return st;
   if ((st = check_heads(num_qo_heads, num_kv_heads))) return st;
   if ((st = check_head_dim_dtype(head_dim, dtype))) return st;
   if (kv_len < 0) return fail(PKV_ERR_INVALID_ARG, "kv_len must be >= 0");
@@ -765,6 +774,7 @@ pkv_status pkv_cascade_run(const pkv_plan_info* plan, const void* q, const pkv_p
                            const int32_t* suffix_indices_d, float sm_scale, void* o, float* lse,
                            void* stream) {
   pkv_status st;
+  if ((st = check_scale(sm_scale))) return st;
   if ((st = check_plan(plan, PKV_KIND_CASCADE))) return st;
   if ((st = check_kv(kv, plan))) return st;
   if (plan->batch == 0) return ok();

@@ -16,8 +16,9 @@
 //   * KV advances in 64-token tiles staged through LDS, double-buffered: the
 //     global loads of tile i+1 are in flight while tile i is computed.
 //     K is stored row-major [token][d] (rows padded to 272 B); V is stored
-//     transposed [d][token] (rows padded to 136 B) so that the PV operand
-//     reads are 8-byte LDS loads.
+//     transposed [d][token] (rows padded to 136 B, columns XOR-swizzled per
+//     16 rows) so that the PV operand reads are 8-byte LDS loads and neither
+//     the staging writes nor the reads have bank conflicts.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_{f16,bf16}: K rows are the A operand
 //     (from LDS), the wave's 32 q rows are the B operand (registers for the
 //     whole item). Lane l then holds 16 scores of row l % 32 per 32 tokens,
@@ -39,6 +40,14 @@ constexpr int KT = 64;                 // KV tokens per tile
 constexpr int KROW = kHeadDim + 8;     // K row stride in LDS (elements)
 constexpr int VROW = KT + 4;           // V^T row stride in LDS (elements)
 constexpr int kTileRows = 128;
+
+// Column (in elements) of logical token column `c` in row `d` of the
+// transposed V tile. The XOR with 4 * (d >> 4) keeps 4-token (8-byte) groups
+// together and makes both access patterns free of LDS bank conflicts: the
+// staging writes (16 lanes writing rows 8 apart, same column) land in 16
+// distinct bank pairs, and the MFMA operand reads (lanes reading 16
+// consecutive rows, same column) still do.
+__device__ __forceinline__ int vt_col(int d, int c) { return c ^ (4 * (d >> 4)); }
 
 // Stores 4 consecutive output values (rounded once to OUT).
 template <class OUT>
@@ -131,8 +140,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       const uint32_t lo23 = __builtin_amdgcn_perm(vst[3][w], vst[2][w], 0x05040100u);
       const uint32_t hi01 = __builtin_amdgcn_perm(vst[1][w], vst[0][w], 0x07060302u);
       const uint32_t hi23 = __builtin_amdgcn_perm(vst[3][w], vst[2][w], 0x07060302u);
-      *reinterpret_cast<u32x2*>(&sV[buf][(8 * sc + 2 * w) * VROW + 4 * sr]) = u32x2{lo01, lo23};
-      *reinterpret_cast<u32x2*>(&sV[buf][(8 * sc + 2 * w + 1) * VROW + 4 * sr]) = u32x2{hi01, hi23};
+      // rows 8*sc + 2w (+1) share (row >> 4) = sc >> 1: see vt_col
+      const int col = vt_col(8 * sc, 4 * sr);
+      *reinterpret_cast<u32x2*>(&sV[buf][(8 * sc + 2 * w) * VROW + col]) = u32x2{lo01, lo23};
+      *reinterpret_cast<u32x2*>(&sV[buf][(8 * sc + 2 * w + 1) * VROW + col]) = u32x2{hi01, hi23};
     }
   };
 
@@ -172,14 +183,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       }
     }
 
-    // Mask (only where the tile reaches past k1 or past this row's causal limit).
+    // Mask (only where the tile reaches past k1 or past this row's causal
+    // limit). The running max is taken on the raw scores and scaled once
+    // (scale > 0), and the scale is folded into the exponent's FMA below.
     const bool need_mask = (tb + KT > k1) || (a.causal && tb + KT - 1 > lim_wave);
     float tmax = neg_inf();
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float x = s[blk][i] * a.scale_log2;
+        float x = s[blk][i];
         if (need_mask) {
           const int t = tb + 32 * blk + 8 * (i >> 2) + 4 * half + (i & 3);
           if (t >= k1 || (a.causal && t > lim)) x = neg_inf();
@@ -187,7 +200,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
         s[blk][i] = x;
         tmax = fmaxf(tmax, x);
       }
-    tmax = max_across_halves(tmax);
+    tmax = max_across_halves(tmax) * a.scale_log2;
     const float m_new = fmaxf(m_run, tmax);
     const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
@@ -202,8 +215,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       const int blk = st >> 1, hf = st & 1;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float x0 = fast_exp2(s[blk][8 * hf + 2 * j] - m_use);
-        const float x1 = fast_exp2(s[blk][8 * hf + 2 * j + 1] - m_use);
+        const float x0 = fast_exp2(fmaf(s[blk][8 * hf + 2 * j], a.scale_log2, -m_use));
+        const float x1 = fast_exp2(fmaf(s[blk][8 * hf + 2 * j + 1], a.scale_log2, -m_use));
         pk[st][j] = T::pack2(x0, x1);
         pqsum = T::add_pair(pk[st][j], pqsum);
         psum += x0 + x1;
@@ -211,17 +224,20 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     }
     l_run = l_run * alpha + psum;
     lq_run = lq_run * alpha + pqsum;
+    // Rescale only when some row's running max moved (wave-uniform branch).
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) acc[mb] *= alpha;
+      for (int mb = 0; mb < 4; ++mb) acc[mb] *= alpha;
+    }
 
     // O^T += V^T P^T over four 16-token steps.
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        const elem* vr = &sV[buf][(32 * mb + lr) * VROW + 16 * st + 4 * half];
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 8);
+        const elem* vrow = &sV[buf][(32 * mb + lr) * VROW];
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + vt_col(32 * mb + lr, 16 * st + 4 * half));
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + vt_col(32 * mb + lr, 16 * st + 4 * half + 8));
         acc[mb] = T::mfma_32x32x16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pk[st], acc[mb]);
       }
     }

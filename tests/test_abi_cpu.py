@@ -157,3 +157,13 @@ def test_cascade_plan_validation(lib):
                                ctypes.byref(info))
     assert st == lib.PKV_ERR_WORKSPACE_TOO_SMALL
     assert info.float_ws_required >= 2 * 2 * 32 * 128 * 4
+
+
+def test_runs_reject_bad_scales(lib):
+    kv = lib.pkv_paged_kv()
+    info = lib.pkv_plan_info()
+    for scale in (0.0, -0.5, float("inf"), float("nan")):
+        assert lib._lib_decode_run(ctypes.byref(info), None, ctypes.byref(kv), None, None, scale,
+                                   None, None, None) == lib.PKV_ERR_INVALID_ARG
+        assert lib._lib_prefill_run(ctypes.byref(info), None, ctypes.byref(kv), None, None, None,
+                                    scale, None, None, None) == lib.PKV_ERR_INVALID_ARG
