@@ -13,12 +13,21 @@
 //   * Workgroup = 4 waves, wave w owns rows 32w .. 32w+31 of the tile; a row
 //     is (query token, query head) with the G heads of a KV group packed
 //     together, so each K/V tile read from HBM serves G heads.
-//   * KV advances in 64-token tiles staged through LDS, double-buffered: the
-//     global loads of tile i+1 are in flight while tile i is computed.
-//     K is stored row-major [token][d] (rows padded to 272 B); V is stored
-//     transposed [d][token] (rows padded to 136 B, columns XOR-swizzled per
-//     16 rows) so that the PV operand reads are 8-byte LDS loads and neither
-//     the staging writes nor the reads have bank conflicts.
+//   * KV advances in 64-token tiles, double-buffered in LDS. The tiles go
+//     from HBM straight into LDS (buffer / global loads with the LDS flag), so
+//     no registers hold them in flight and no instructions copy them: wave w
+//     fetches the 16-token group w of the next tile (four 1 KB loads for K,
+//     four for V) while every wave computes the current one. The page id of a
+//     group is read one tile before its loads are issued. With page_size a
+//     multiple of 16 a group lies in one page: one descriptor per wave and
+//     tile, ranged to the group's valid tokens so that tokens past the item
+//     read as zero; other page sizes look up every token and repeat the last
+//     valid one past the end (its weight is exactly 0).
+//   * LDS rows are 256 B (one token's 128 values, unpadded) with the 16-byte
+//     chunks XOR-swizzled per row: K by (row mod 16), V by 4 * (row mod 4).
+//     Neither the K operand reads (32 rows, one chunk) nor the transposing V
+//     reads (ds_read_b64_tr_b16: 4 rows x 16 values per 16 lanes) then hit a
+//     bank twice in one cycle.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_{f16,bf16}: K rows are the A operand
 //     (from LDS), the wave's 32 q rows are the B operand (registers for the
 //     whole item). Lane l then holds 16 scores of row l % 32 per 32 tokens,
@@ -36,18 +45,36 @@ namespace pkv {
 
 namespace {
 
-constexpr int KT = 64;                 // KV tokens per tile
-constexpr int KROW = kHeadDim + 8;     // K row stride in LDS (elements)
-constexpr int VROW = KT + 4;           // V^T row stride in LDS (elements)
+constexpr int KT = 64;                       // KV tokens per tile
 constexpr int kTileRows = 128;
+constexpr int kRowBytes = kHeadDim * 2;      // one token row in LDS
+constexpr int kTileBytes = KT * kRowBytes;   // 16 KB per K or V tile
 
-// Column (in elements) of logical token column `c` in row `d` of the
-// transposed V tile. The XOR with 4 * (d >> 4) keeps 4-token (8-byte) groups
-// together and makes both access patterns free of LDS bank conflicts: the
-// staging writes (16 lanes writing rows 8 apart, same column) land in 16
-// distinct bank pairs, and the MFMA operand reads (lanes reading 16
-// consecutive rows, same column) still do.
-__device__ __forceinline__ int vt_col(int d, int c) { return c ^ (4 * (d >> 4)); }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Byte offset in an LDS tile of 16-byte chunk c of token row t.
+__device__ __forceinline__ int k_at(int t, int c) { return t * kRowBytes + 16 * (c ^ (t & 15)); }
+__device__ __forceinline__ int v_at(int t, int c) { return t * kRowBytes + 16 * (c ^ (4 * (t & 3))); }
+
+// 16 bytes per lane from global memory straight into LDS: lane i writes
+// dst + 16 i (dst wave-uniform). Buffer form: bytes past the descriptor's
+// range read as zero. Non-temporal: the KV tile is read once per workgroup.
+__device__ __forceinline__ void buffer_to_lds_16B(__amdgpu_buffer_rsrc_t r, lds_void* dst,
+                                                  uint32_t byte_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, byte_off, 0, 0, kCacheStream);
+}
+__device__ __forceinline__ void global_to_lds_16B(const void* src, lds_void* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, kCacheStream);
+}
+__device__ __forceinline__ s16x4 lds_read_tr16_b64(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+}
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left free): the direct-to-LDS loads
+// of this wave have landed.
+__device__ __forceinline__ void wait_lds_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Stores 4 consecutive output values (rounded once to OUT).
 template <class OUT>
@@ -67,11 +94,17 @@ template <class T, class OUT, int MODE>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   using elem = typename T::elem;
   constexpr int D = kHeadDim;
-  __shared__ __attribute__((aligned(16))) elem sK[2][KT * KROW];
-  __shared__ __attribute__((aligned(16))) elem sV[2][D * VROW];
+  // Two stages, four distinct arrays: the compiler then sees that the loads
+  // into one stage never alias the operand reads of the other and does not
+  // wait for the loads in flight before reading the current tile.
+  __shared__ __attribute__((aligned(1024))) char sKa[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sVa[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sKb[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sVb[kTileBytes];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, half = lane >> 5;
   const int G = a.group;
 
@@ -100,50 +133,70 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     for (int kk = 0; kk < 8; ++kk) qv[kk] = row_ok ? load_16B(qp + 16 * kk) : u32x4{0, 0, 0, 0};
   }
 
-  const elem* kbase = static_cast<const elem*>(a.k) + static_cast<int64_t>(g) * a.head_stride;
-  const elem* vbase = static_cast<const elem*>(a.v) + static_cast<int64_t>(g) * a.head_stride;
-  const int32_t* pages = a.kv_indices + a.kv_indptr[b];
+  // ---- staging: wave w fetches token rows 16w .. 16w+15 of a tile; load j
+  // (0..3) covers rows 16w + 4j + lane/16, lane % 16 being the LDS chunk slot.
+  const char* kbase = static_cast<const char*>(a.k) + static_cast<int64_t>(g) * a.head_stride * 2;
+  const char* vbase = static_cast<const char*>(a.v) + static_cast<int64_t>(g) * a.head_stride * 2;
   const int P = a.page_size;
-  auto token_off = [&](int t) -> int64_t {
-    const int pi = t / P;
-    const int sl = t - pi * P;
-    return static_cast<int64_t>(pages[pi]) * a.page_stride +
-           static_cast<int64_t>(sl) * a.token_stride;
+  const int64_t ps_bytes = a.page_stride * 2;
+  const uint32_t ts_bytes = static_cast<uint32_t>(a.token_stride) * 2;
+  const int page0 = a.kv_indptr[b];
+  const int npages = a.kv_indptr[b + 1] - page0;
+  const __amdgpu_buffer_rsrc_t pt = make_rsrc(a.kv_indices + page0, 4u * static_cast<uint32_t>(npages));
+  const int srow = lane >> 4, spos = lane & 15;
+  // Global chunk fetched by this lane for load j (the inverse of the swizzle).
+  auto k_chunk = [&](int j) { return spos ^ (4 * j + srow); };
+  const int v_chunk = spos ^ (4 * srow);
+  auto lds_dst = [&](char* tile_base, int j) -> lds_void* {
+    return (lds_void*)(tile_base + (16 * wave + 4 * j) * kRowBytes);
   };
 
-  // Staging: K thread (c = tid % 16 d-chunk, tokens tid/16 + 16*rep);
-  //          V thread (c = tid % 16 d-chunk, tokens 4*(tid/16) + u).
-  const int sc = tid & 15, sr = tid >> 4;
-  u32x4 kst[4], vst[4];
-  auto stage_load = [&](int tb) {
-    const int last = k1 - 1;
+  // Page-uniform mode: page id of the group of tile ti (wave-uniform).
+  const int pshift = (P & (P - 1)) == 0 ? __builtin_ctz(P) : -1;
+  auto group_page = [&](int ti) -> int {      // page index in the request
+    const int tc = min(k0 + ti * KT + 16 * wave, k1 - 1);
+    // (uniform; readfirstlane keeps it in SGPRs when the division runs on VALU)
+    return __builtin_amdgcn_readfirstlane(pshift >= 0 ? (tc >> pshift) : tc / P);
+  };
+  // Generic mode: page index and slot of the lane's token for load j of tile ti.
+  auto lane_token = [&](int ti, int j) -> int { return min(k0 + ti * KT + 16 * wave + 4 * j + srow, k1 - 1); };
+
+  int pid_next[4];   // page ids for the next tile's loads (uniform mode: [0] only)
+  auto fetch_pids = [&](int ti) {
+    if constexpr (MODE == kPagedUniform) {
+      pid_next[0] = __builtin_amdgcn_raw_buffer_load_b32(pt, 4u * group_page(ti), 0, 0);
+    } else {
 #pragma unroll
-    for (int rep = 0; rep < 4; ++rep) {
-      const int t = min(tb + sr + 16 * rep, last);
-      kst[rep] = load_16B(kbase + token_off(t) + 8 * sc);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = min(tb + 4 * sr + u, last);
-      vst[u] = load_16B(vbase + token_off(t) + 8 * sc);
+      for (int j = 0; j < 4; ++j)
+        pid_next[j] = __builtin_amdgcn_raw_buffer_load_b32(pt, 4u * (lane_token(ti, j) / P), 0, 0);
     }
   };
-  auto stage_store = [&](int buf) {
+  auto issue_tile = [&](int ti, char* kdst, char* vdst) {
+    if constexpr (MODE == kPagedUniform) {
+      const int t = k0 + ti * KT + 16 * wave;
+      const int pi = group_page(ti);
+      const int pid = __builtin_amdgcn_readfirstlane(pid_next[0]);
+      const int sl = min(t, k1 - 1) - pi * P;
+      const int nvalid = __builtin_amdgcn_readfirstlane(max(0, min(16, k1 - t)));   // (v_med3)
+      const int64_t goff = static_cast<int64_t>(pid) * ps_bytes + static_cast<int64_t>(sl) * ts_bytes;
+      const uint32_t nbytes = static_cast<uint32_t>(nvalid) * ts_bytes;
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + goff, nbytes);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + goff, nbytes);
 #pragma unroll
-    for (int rep = 0; rep < 4; ++rep)
-      *reinterpret_cast<u32x4*>(&sK[buf][(sr + 16 * rep) * KROW + 8 * sc]) = kst[rep];
-    // Transpose 4 tokens x 8 d into 8 rows of V^T (4 tokens each).
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t row = static_cast<uint32_t>(4 * j + srow) * ts_bytes;
+        buffer_to_lds_16B(rk, lds_dst(kdst, j), row + 16 * k_chunk(j));
+        buffer_to_lds_16B(rv, lds_dst(vdst, j), row + 16 * v_chunk);
+      }
+    } else {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // d = 8*sc + 2w (low halves) and 8*sc + 2w + 1 (high halves)
-      const uint32_t lo01 = __builtin_amdgcn_perm(vst[1][w], vst[0][w], 0x05040100u);
-      const uint32_t lo23 = __builtin_amdgcn_perm(vst[3][w], vst[2][w], 0x05040100u);
-      const uint32_t hi01 = __builtin_amdgcn_perm(vst[1][w], vst[0][w], 0x07060302u);
-      const uint32_t hi23 = __builtin_amdgcn_perm(vst[3][w], vst[2][w], 0x07060302u);
-      // rows 8*sc + 2w (+1) share (row >> 4) = sc >> 1: see vt_col
-      const int col = vt_col(8 * sc, 4 * sr);
-      *reinterpret_cast<u32x2*>(&sV[buf][(8 * sc + 2 * w) * VROW + col]) = u32x2{lo01, lo23};
-      *reinterpret_cast<u32x2*>(&sV[buf][(8 * sc + 2 * w + 1) * VROW + col]) = u32x2{hi01, hi23};
+      for (int j = 0; j < 4; ++j) {
+        const int tc = lane_token(ti, j);
+        const int sl = tc - (tc / P) * P;
+        const int64_t off = static_cast<int64_t>(pid_next[j]) * ps_bytes + static_cast<int64_t>(sl) * ts_bytes;
+        global_to_lds_16B(kbase + off + 16 * k_chunk(j), lds_dst(kdst, j));
+        global_to_lds_16B(vbase + off + 16 * v_chunk, lds_dst(vdst, j));
+      }
     }
   };
 
@@ -158,16 +211,28 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
 
   const int ntiles = (k1 - k0 + KT - 1) / KT;
   if (ntiles > 0) {
-    stage_load(k0);
-    stage_store(0);
+    fetch_pids(0);
+    issue_tile(0, sKa, sVa);   // waits for the page ids it needs
+    fetch_pids(1);
   }
+  wait_lds_loads();
   __syncthreads();
 
-  for (int ti = 0; ti < ntiles; ++ti) {
-    const int buf = ti & 1;
+  // Operand addresses that do not depend on the tile.
+  // K (A operand of S^T): row 32blk + lr, chunk 2kk + half.
+  // V (A operand of O^T, transposing read): 16-lane group q16 = lane/16 reads
+  // rows base + (lane%16)/4 at d = 32mb + 16(q16 & 1) + 4(lane & 3).
+  const int vq = (lane >> 2) & 3;                           // row within the 4-row block
+  const int vchunk_lo = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+  const int vbyte = 8 * (lane & 1);
+
+  // One tile: compute from (kt, vt) while the next tile streams into (kn, vn).
+  auto step = [&](int ti, const char* kt, const char* vt, char* kn, char* vn) {
     const int tb = k0 + ti * KT;
-    const bool more = ti + 1 < ntiles;
-    if (more) stage_load(tb + KT);
+    if (ti + 1 < ntiles) {
+      issue_tile(ti + 1, kn, vn);
+      fetch_pids(ti + 2);
+    }
 
     // S^T for two 32-token blocks.
     f32x16 s[2];
@@ -177,8 +242,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       for (int i = 0; i < 16; ++i) s[blk][i] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(
-            &sK[buf][(32 * blk + lr) * KROW + 16 * kk + 8 * half]);
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(kt + k_at(32 * blk + lr, 2 * kk + half));
         s[blk] = T::mfma_32x32x16(kf, qv[kk], s[blk]);
       }
     }
@@ -230,20 +294,28 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       for (int mb = 0; mb < 4; ++mb) acc[mb] *= alpha;
     }
 
-    // O^T += V^T P^T over four 16-token steps.
+    // O^T += V^T P^T over four 16-token steps. Step st covers tokens
+    // 16st + 4*half + {0..3} (first read) and + {8..11} (second read), the
+    // order in which pk[st] holds them.
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
+      const int r0 = 16 * st + 4 * half + vq;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        const elem* vrow = &sV[buf][(32 * mb + lr) * VROW];
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + vt_col(32 * mb + lr, 16 * st + 4 * half));
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + vt_col(32 * mb + lr, 16 * st + 4 * half + 8));
-        acc[mb] = T::mfma_32x32x16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pk[st], acc[mb]);
+        const int c = 4 * mb + vchunk_lo;
+        const s16x4 lo = lds_read_tr16_b64(vt + v_at(r0, c) + vbyte);
+        const s16x4 hi = lds_read_tr16_b64(vt + v_at(r0 + 8, c) + vbyte);
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        acc[mb] = T::mfma_32x32x16(u32x4{l2[0], l2[1], h2[0], h2[1]}, pk[st], acc[mb]);
       }
     }
 
-    if (more) stage_store(buf ^ 1);
+    wait_lds_loads();
     __syncthreads();
+  };
+  for (int ti = 0; ti < ntiles; ti += 2) {
+    step(ti, sKa, sVa, sKb, sVb);
+    if (ti + 1 < ntiles) step(ti + 1, sKb, sVb, sKa, sVa);
   }
 
   // Finalize row lr.
@@ -265,8 +337,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       }
     if (half == 0 && a.lse != nullptr) a.lse[orow] = lse;
   } else {
-    const int64_t srow = static_cast<int64_t>(slot) * kTileRows + 32 * wave + lr;
-    float* po = a.part_o + srow * D;
+    const int64_t srow_out = static_cast<int64_t>(slot) * kTileRows + 32 * wave + lr;
+    float* po = a.part_o + srow_out * D;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -276,13 +348,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
             f32x4{acc[mb][4 * q4] * inv, acc[mb][4 * q4 + 1] * inv, acc[mb][4 * q4 + 2] * inv,
                   acc[mb][4 * q4 + 3] * inv};
       }
-    if (half == 0) a.part_lse[srow] = lse;
+    if (half == 0) a.part_lse[srow_out] = lse;
   }
 }
 
 template <class T, class OUT>
-hipError_t launch_prefill_t(const PrefillArgs& a, int32_t grid, hipStream_t s) {
-  hipLaunchKernelGGL((prefill_kernel<T, OUT, kPagedGeneric>), dim3(grid), dim3(256), 0, s, a);
+hipError_t launch_prefill_t(const PrefillArgs& a, PageMode mode, int32_t grid, hipStream_t s) {
+  if (mode == kPagedUniform)
+    hipLaunchKernelGGL((prefill_kernel<T, OUT, kPagedUniform>), dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<T, OUT, kPagedGeneric>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -291,21 +366,21 @@ hipError_t launch_prefill_t(const PrefillArgs& a, int32_t grid, hipStream_t s) {
 int32_t prefill_occupancy() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&prefill_kernel<BF16, __bf16, kPagedGeneric>), 256,
+          &n, reinterpret_cast<const void*>(&prefill_kernel<BF16, __bf16, kPagedUniform>), 256,
           0) != hipSuccess)
     return 0;
   return n;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int32_t storage_dtype, OutKind out,
-                          PageMode /*mode*/, int32_t grid, hipStream_t stream) {
+                          PageMode mode, int32_t grid, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
   if (storage_dtype == 0) {
-    return out == kOutF32 ? launch_prefill_t<F16, float>(a, grid, stream)
-                          : launch_prefill_t<F16, _Float16>(a, grid, stream);
+    return out == kOutF32 ? launch_prefill_t<F16, float>(a, mode, grid, stream)
+                          : launch_prefill_t<F16, _Float16>(a, mode, grid, stream);
   }
-  return out == kOutF32 ? launch_prefill_t<BF16, float>(a, grid, stream)
-                        : launch_prefill_t<BF16, __bf16>(a, grid, stream);
+  return out == kOutF32 ? launch_prefill_t<BF16, float>(a, mode, grid, stream)
+                        : launch_prefill_t<BF16, __bf16>(a, mode, grid, stream);
 }
 
 }  // namespace pkv
