@@ -58,15 +58,19 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 __device__ __forceinline__ int k_at(int t, int c) { return t * kRowBytes + 16 * (c ^ (t & 15)); }
 __device__ __forceinline__ int v_at(int t, int c) { return t * kRowBytes + 16 * (c ^ (4 * (t & 3))); }
 
+// Cache policy of the KV tile loads. Every query tile of a (request, KV
+// head) reads the same KV, so the tiles stay cacheable.
+constexpr int kKvPolicy = kCacheDefault;
+
 // 16 bytes per lane from global memory straight into LDS: lane i writes
 // dst + 16 i (dst wave-uniform). Buffer form: bytes past the descriptor's
-// range read as zero. Non-temporal: the KV tile is read once per workgroup.
+// range read as zero.
 __device__ __forceinline__ void buffer_to_lds_16B(__amdgpu_buffer_rsrc_t r, lds_void* dst,
                                                   uint32_t byte_off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, byte_off, 0, 0, kCacheStream);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, byte_off, 0, 0, kKvPolicy);
 }
 __device__ __forceinline__ void global_to_lds_16B(const void* src, lds_void* dst) {
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, kCacheStream);
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, kKvPolicy);
 }
 __device__ __forceinline__ s16x4 lds_read_tr16_b64(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
@@ -251,19 +255,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     // limit). The running max is taken on the raw scores and scaled once
     // (scale > 0), and the scale is folded into the exponent's FMA below.
     const bool need_mask = (tb + KT > k1) || (a.causal && tb + KT - 1 > lim_wave);
+    if (need_mask) {
+      // Last key this lane's row may see in the tile, relative to the
+      // lane's first token (one compare and select per score, no branches).
+      const int tlast = (a.causal ? min(k1 - 1, lim) : k1 - 1) - (tb + 4 * half);
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * blk + 8 * (i >> 2) + (i & 3) > tlast) s[blk][i] = neg_inf();
+    }
     float tmax = neg_inf();
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = s[blk][i];
-        if (need_mask) {
-          const int t = tb + 32 * blk + 8 * (i >> 2) + 4 * half + (i & 3);
-          if (t >= k1 || (a.causal && t > lim)) x = neg_inf();
-        }
-        s[blk][i] = x;
-        tmax = fmaxf(tmax, x);
-      }
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[blk][i]);
     tmax = max_across_halves(tmax) * a.scale_log2;
     const float m_new = fmaxf(m_run, tmax);
     const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
