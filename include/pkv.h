@@ -77,7 +77,10 @@ enum { PKV_KIND_DECODE = 1, PKV_KIND_PREFILL = 2, PKV_KIND_CASCADE = 3 };
 /* A paged K/V cache. k and v are separate device bases with one set of
  * strides (in elements), which also covers an interleaved [pages, 2, P, H, D]
  * pool. head_dim elements of one (page, slot, head) are contiguous. All
- * strides must be multiples of 8 elements and k, v 16-byte aligned. */
+ * strides must be multiples of 8 elements and k, v 16-byte aligned;
+ * token_stride is below 2^26 and page_stride below 2^30 elements (the kernels
+ * form a page's byte offset in 32 bits and multiply it by the page id in 64).
+ * Otherwise the run calls return PKV_ERR_INVALID_ARG. */
 typedef struct pkv_paged_kv {
   const void* k;
   const void* v;

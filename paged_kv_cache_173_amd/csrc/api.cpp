@@ -132,6 +132,8 @@ pkv_status check_kv(const pkv_paged_kv* kv, const pkv_plan_info* plan) {
     return fail(PKV_ERR_INVALID_ARG, "k / v must be 16-byte aligned");
   if (kv->token_stride < kv->head_dim || kv->token_stride > (INT32_MAX / 32))
     return fail(PKV_ERR_INVALID_ARG, "token_stride must be in [head_dim, 2^26)");
+  if (kv->page_stride >= (int64_t{1} << 30))
+    return fail(PKV_ERR_INVALID_ARG, "page_stride must be below 2^30 elements");
   return PKV_OK;
 }
 

@@ -38,6 +38,8 @@
 //     accumulator of row l % 32 stays in lane l, so the rescale is lane-local.
 //   * The scale multiplies the fp32 scores (q is not pre-scaled), in the
 //     log2 domain; LSE = (m + log2 l) * ln 2.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -45,10 +47,10 @@ namespace pkv {
 
 namespace {
 
-constexpr int KT = 64;                       // KV tokens per tile
+constexpr int KT = 32;                       // KV tokens per tile
 constexpr int kTileRows = 128;
 constexpr int kRowBytes = kHeadDim * 2;      // one token row in LDS
-constexpr int kTileBytes = KT * kRowBytes;   // 16 KB per K or V tile
+constexpr int kTileBytes = KT * kRowBytes;   // 8 KB per K or V tile
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -76,9 +78,25 @@ __device__ __forceinline__ s16x4 lds_read_tr16_b64(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
 }
 
-// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left free): the direct-to-LDS loads
-// of this wave have landed.
-__device__ __forceinline__ void wait_lds_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left free): at most N of this wave's
+// vector-memory loads (direct-to-LDS loads included; they count in issue
+// order) are still in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier for the LDS tiles without a memory fence: the wave's own
+// LDS reads are complete (lgkmcnt(0)) and the direct-to-LDS loads it needs
+// were waited for by the caller, so no vector-memory wait is forced here (a
+// fence would wait for every load in flight, including the prefetches).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Stores 4 consecutive output values (rounded once to OUT).
 template <class OUT>
@@ -94,17 +112,41 @@ __device__ __forceinline__ void store4(OUT* p, float x0, float x1, float x2, flo
   }
 }
 
+// Lazy rescaling: the exponent reference of a row moves only when the row's
+// scaled maximum exceeds it by more than this many powers of two, so weights
+// stay <= 2^8 (exact in fp32 and in the fp16 / bf16 range) and the running
+// state is rescaled a few times per row instead of on most tiles.
+constexpr float kRescaleSlack = 8.f;
+
 template <class T, class OUT, int MODE>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   using elem = typename T::elem;
   constexpr int D = kHeadDim;
-  // Two stages, four distinct arrays: the compiler then sees that the loads
-  // into one stage never alias the operand reads of the other and does not
-  // wait for the loads in flight before reading the current tile.
-  __shared__ __attribute__((aligned(1024))) char sKa[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char sVa[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char sKb[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char sVb[kTileBytes];
+  // K and V tiles in LDS, four buffers each: tile t lives in buffer t % 4.
+  // Eight distinct arrays, so the compiler sees that the loads streaming into
+  // one buffer never alias the operand reads of another.
+  __shared__ __attribute__((aligned(1024))) char sK0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sK1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sK2[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sK3[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sV0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sV1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sV2[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char sV3[kTileBytes];
+  auto kbuf = [&](auto ph) -> char* {
+    constexpr int i = decltype(ph)::value & 3;
+    if constexpr (i == 0) return sK0;
+    else if constexpr (i == 1) return sK1;
+    else if constexpr (i == 2) return sK2;
+    else return sK3;
+  };
+  auto vbuf = [&](auto ph) -> char* {
+    constexpr int i = decltype(ph)::value & 3;
+    if constexpr (i == 0) return sV0;
+    else if constexpr (i == 1) return sV1;
+    else if constexpr (i == 2) return sV2;
+    else return sV3;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -127,6 +169,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   // Smallest causal limit of the wave (its first row): tiles that end at or
   // before it need no causal mask for any row of the wave.
   const int lim_wave = (tile * kTileRows + 32 * wave) / G + L - Q;
+  // Keys past this one need a mask for some row of the wave (the causal
+  // limit of the wave's first row, or the item's end).
+  const int mask_from = a.causal ? min(k1 - 1, lim_wave) : k1 - 1;
 
   // q^T as the B operand: lane holds q[row lr][d = 16kk + 8*half .. +7].
   u32x4 qv[8];
@@ -137,199 +182,362 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
     for (int kk = 0; kk < 8; ++kk) qv[kk] = row_ok ? load_16B(qp + 16 * kk) : u32x4{0, 0, 0, 0};
   }
 
-  // ---- staging: wave w fetches token rows 16w .. 16w+15 of a tile; load j
-  // (0..3) covers rows 16w + 4j + lane/16, lane % 16 being the LDS chunk slot.
+  // ---- staging: wave w fetches token rows 8w .. 8w+7 of a tile; load j
+  // (0..1) covers rows 8w + 4j + lane/16, lane % 16 being the LDS chunk slot.
   const char* kbase = static_cast<const char*>(a.k) + static_cast<int64_t>(g) * a.head_stride * 2;
   const char* vbase = static_cast<const char*>(a.v) + static_cast<int64_t>(g) * a.head_stride * 2;
   const int P = a.page_size;
-  const int64_t ps_bytes = a.page_stride * 2;
+  const uint32_t ps_bytes = static_cast<uint32_t>(a.page_stride) * 2;   // < 2^31 (checked on the host)
   const uint32_t ts_bytes = static_cast<uint32_t>(a.token_stride) * 2;
   const int page0 = a.kv_indptr[b];
   const int npages = a.kv_indptr[b + 1] - page0;
   const __amdgpu_buffer_rsrc_t pt = make_rsrc(a.kv_indices + page0, 4u * static_cast<uint32_t>(npages));
   const int srow = lane >> 4, spos = lane & 15;
   // Global chunk fetched by this lane for load j (the inverse of the swizzle).
-  auto k_chunk = [&](int j) { return spos ^ (4 * j + srow); };
+  auto k_chunk = [&](int j) { return spos ^ (8 * (wave & 1) + 4 * j + srow); };
   const int v_chunk = spos ^ (4 * srow);
   auto lds_dst = [&](char* tile_base, int j) -> lds_void* {
-    return (lds_void*)(tile_base + (16 * wave + 4 * j) * kRowBytes);
+    return (lds_void*)(tile_base + (8 * wave + 4 * j) * kRowBytes);
   };
 
-  // Page-uniform mode: page id of the group of tile ti (wave-uniform).
-  const int pshift = (P & (P - 1)) == 0 ? __builtin_ctz(P) : -1;
-  auto group_page = [&](int ti) -> int {      // page index in the request
-    const int tc = min(k0 + ti * KT + 16 * wave, k1 - 1);
-    // (uniform; readfirstlane keeps it in SGPRs when the division runs on VALU)
-    return __builtin_amdgcn_readfirstlane(pshift >= 0 ? (tc >> pshift) : tc / P);
+  // Page-uniform mode (page_size a power of two >= 16): page index (in the
+  // request) of the wave's 8-token group of tile ti. Item starts are page
+  // aligned, so a group never straddles a page; the token is clamped into the
+  // item, so the index is in range.
+  const int pshift = __builtin_ctz(static_cast<unsigned>(P));
+  auto group_page = [&](int ti) -> int {
+    const int tc = min(k0 + ti * KT + 8 * wave, k1 - 1);
+    return tc >> pshift;
   };
-  // Generic mode: page index and slot of the lane's token for load j of tile ti.
-  auto lane_token = [&](int ti, int j) -> int { return min(k0 + ti * KT + 16 * wave + 4 * j + srow, k1 - 1); };
+  // Generic mode: the lane's token for load j of tile ti (clamped likewise).
+  auto lane_token = [&](int ti, int j) -> int { return min(k0 + ti * KT + 8 * wave + 4 * j + srow, k1 - 1); };
 
-  int pid_next[4];   // page ids for the next tile's loads (uniform mode: [0] only)
-  auto fetch_pids = [&](int ti) {
+  // Page ids of one tile's loads, fetched two iterations before they are
+  // used: vector-memory loads complete in issue order, so a consumer of an id
+  // waits for every load issued before it, and two iterations is when the
+  // tile loads issued just before it are due anyway. Uniform mode: the group's
+  // id (wave-uniform); generic mode: the ids of the lane's two tokens. Loads
+  // past the page list read zero (the descriptor's range).
+  struct Pids { int p[2]; };
+  auto fetch_pids = [&](int ti) -> Pids {
+    Pids r;
     if constexpr (MODE == kPagedUniform) {
-      pid_next[0] = __builtin_amdgcn_raw_buffer_load_b32(pt, 4u * group_page(ti), 0, 0);
+      r.p[0] = __builtin_amdgcn_raw_buffer_load_b32(pt, 0, 4u * group_page(ti), 0);
+      r.p[1] = 0;
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        pid_next[j] = __builtin_amdgcn_raw_buffer_load_b32(pt, 4u * (lane_token(ti, j) / P), 0, 0);
+      for (int j = 0; j < 2; ++j)
+        r.p[j] = __builtin_amdgcn_raw_buffer_load_b32(pt, 4u * (lane_token(ti, j) / P), 0, 0);
+    }
+    return r;
+  };
+  // Where the wave's group of a tile sits in the pool (uniform mode): its
+  // byte offset from the K / V base and its number of valid bytes (tokens
+  // past the item read as zero). K and V of a tile share it.
+  struct Group { uint64_t off; uint32_t nbytes; };
+  auto group_of = [&](int ti, const Pids& pid) -> Group {
+    const int t = k0 + ti * KT + 8 * wave;
+    const uint32_t id = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(pid.p[0]));
+    const uint32_t sl = static_cast<uint32_t>(min(t, k1 - 1) & (P - 1));
+    // clamp(k1 - t, 0, 8): wave-uniform (readfirstlane: the compiler forms the
+    // clamp with a vector med3)
+    const uint32_t nvalid = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(max(0, min(8, k1 - t))));
+    return {static_cast<uint64_t>(id) * ps_bytes + sl * ts_bytes, nvalid * ts_bytes};
+  };
+  auto issue_group = [&](const Group& gr, const char* base, char* dst, bool is_k) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + gr.off, gr.nbytes);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t row = static_cast<uint32_t>(4 * j + srow) * ts_bytes;
+      buffer_to_lds_16B(r, lds_dst(dst, j), row + 16 * (is_k ? k_chunk(j) : v_chunk));
     }
   };
-  auto issue_tile = [&](int ti, char* kdst, char* vdst) {
+  // Loads K (is_k) or V of tile ti into dst.
+  auto issue = [&](int ti, const Pids& pid, const char* base, char* dst, bool is_k) {
     if constexpr (MODE == kPagedUniform) {
-      const int t = k0 + ti * KT + 16 * wave;
-      const int pi = group_page(ti);
-      const int pid = __builtin_amdgcn_readfirstlane(pid_next[0]);
-      const int sl = min(t, k1 - 1) - pi * P;
-      const int nvalid = __builtin_amdgcn_readfirstlane(max(0, min(16, k1 - t)));   // (v_med3)
-      const int64_t goff = static_cast<int64_t>(pid) * ps_bytes + static_cast<int64_t>(sl) * ts_bytes;
-      const uint32_t nbytes = static_cast<uint32_t>(nvalid) * ts_bytes;
-      const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + goff, nbytes);
-      const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + goff, nbytes);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t row = static_cast<uint32_t>(4 * j + srow) * ts_bytes;
-        buffer_to_lds_16B(rk, lds_dst(kdst, j), row + 16 * k_chunk(j));
-        buffer_to_lds_16B(rv, lds_dst(vdst, j), row + 16 * v_chunk);
-      }
+      issue_group(group_of(ti, pid), base, dst, is_k);
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 2; ++j) {
         const int tc = lane_token(ti, j);
         const int sl = tc - (tc / P) * P;
-        const int64_t off = static_cast<int64_t>(pid_next[j]) * ps_bytes + static_cast<int64_t>(sl) * ts_bytes;
-        global_to_lds_16B(kbase + off + 16 * k_chunk(j), lds_dst(kdst, j));
-        global_to_lds_16B(vbase + off + 16 * v_chunk, lds_dst(vdst, j));
+        const uint64_t off = static_cast<uint64_t>(static_cast<uint32_t>(pid.p[j])) * ps_bytes + sl * ts_bytes;
+        global_to_lds_16B(base + off + 16 * (is_k ? k_chunk(j) : v_chunk), lds_dst(dst, j));
       }
     }
   };
 
-  float m_run = neg_inf();   // running max of row lr (log2 domain)
-  float l_run = 0.f;         // this lane's share of the running sum (exact weights)
-  float lq_run = 0.f;        // the same sum over the rounded weights fed to the PV MFMA
-  f32x16 acc[4];             // acc[mb][i]: row lr, d = 32mb + 8(i/4) + 4*half + i%4
+  // Row state. The exponent reference m_ref (log2 domain, scaled) is the row
+  // maximum seen so far up to the lazy slack; weights are
+  // exp2(scale_log2 * s - m_ref) rounded once to the storage dtype, and both
+  // the normalisation of O and the LSE use the sum of those rounded weights
+  // (O is then an exact convex combination of V rows).
+  float m_ref = neg_inf();
+  float neg_m = 0.f;          // -m_ref, or 0 while m_ref = -inf
+  // Raw-score threshold (m_ref + slack) / scale_log2: a tile needs the
+  // rescale path only if some lane holds a score above it (any rounding in
+  // it only moves the point at which the reference is refreshed).
+  float thr = neg_inf();
+  const float inv_scale_log2 = 1.f / a.scale_log2;
+  float l_run = 0.f;          // this lane's share of the row's weight sum
+  f32x16 acc[4];              // acc[mb][i]: row lr, d = 32mb + 8(i/4) + 4*half + i%4
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
 
   const int ntiles = (k1 - k0 + KT - 1) / KT;
-  if (ntiles > 0) {
-    fetch_pids(0);
-    issue_tile(0, sKa, sVa);   // waits for the page ids it needs
-    fetch_pids(1);
-  }
-  wait_lds_loads();
-  __syncthreads();
 
-  // Operand addresses that do not depend on the tile.
-  // K (A operand of S^T): row 32blk + lr, chunk 2kk + half.
-  // V (A operand of O^T, transposing read): 16-lane group q16 = lane/16 reads
-  // rows base + (lane%16)/4 at d = 32mb + 16(q16 & 1) + 4(lane & 3).
-  const int vq = (lane >> 2) & 3;                           // row within the 4-row block
+  // Operand addresses. Both swizzles only permute 16-byte chunks inside a
+  // row, so every read address of a tile is one per-lane base XOR a constant:
+  //  * K (A operand of S^T): row lr, chunk 2kk + half, stored at chunk
+  //    (2kk + half) ^ (lr & 15): byte lr*256 + 16*(half ^ (lr & 15)), XOR 32kk.
+  //  * V (A operand of O^T, transposing read): 16-lane group q16 = lane/16
+  //    reads row 16st + 4*half + vq (+8 for the second read), vq = (lane/4)&3,
+  //    at d = 32mb + 16(q16 & 1) + 4(lane & 3): chunk 4mb + vchunk_lo stored
+  //    at chunk (4mb + vchunk_lo) ^ 4vq: byte (4*half + vq)*256 +
+  //    16*vchunk_lo + 8*(lane & 1) + 64*vq, XOR 64mb, plus 4096st (+2048).
+  // The twelve per-lane offsets live in registers; a buffer's base (and the
+  // 16-token step, +4096, and the +8 rows, +2048, of the V reads) is the
+  // instruction's immediate offset.
+  const int k_lane = lr * kRowBytes + 16 * (half ^ (lr & 15));
+  const int vq = (lane >> 2) & 3;
   const int vchunk_lo = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-  const int vbyte = 8 * (lane & 1);
+  const int v_lane = (4 * half + vq) * kRowBytes + 16 * vchunk_lo + 8 * (lane & 1) + 64 * vq;
+  int ka[8], va[4];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) ka[kk] = k_lane ^ (32 * kk);
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) va[mb] = v_lane ^ (64 * mb);
 
-  // One tile: compute from (kt, vt) while the next tile streams into (kn, vn).
-  auto step = [&](int ti, const char* kt, const char* vt, char* kn, char* vn) {
+  // S^T of one tile: K rows are the A operand (LDS), q^T the B operand.
+  auto qk = [&](const char* kt, f32x16& s) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const u32x4 kf = *reinterpret_cast<const u32x4*>(kt + ka[kk]);
+      s = T::mfma_32x32x16(kf, qv[kk], s);
+    }
+  };
+  // Masks tile ti's scores where the tile reaches past k1 or past the row's
+  // causal limit (wave-uniform test; one compare and select per score).
+  auto mask = [&](int ti, f32x16& s) {
     const int tb = k0 + ti * KT;
-    if (ti + 1 < ntiles) {
-      issue_tile(ti + 1, kn, vn);
-      fetch_pids(ti + 2);
-    }
-
-    // S^T for two 32-token blocks.
-    f32x16 s[2];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[blk][i] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const u32x4 kf = *reinterpret_cast<const u32x4*>(kt + k_at(32 * blk + lr, 2 * kk + half));
-        s[blk] = T::mfma_32x32x16(kf, qv[kk], s[blk]);
-      }
-    }
-
-    // Mask (only where the tile reaches past k1 or past this row's causal
-    // limit). The running max is taken on the raw scores and scaled once
-    // (scale > 0), and the scale is folded into the exponent's FMA below.
-    const bool need_mask = (tb + KT > k1) || (a.causal && tb + KT - 1 > lim_wave);
-    if (need_mask) {
-      // Last key this lane's row may see in the tile, relative to the
-      // lane's first token (one compare and select per score, no branches).
+    if (tb + KT - 1 > mask_from) {
       const int tlast = (a.causal ? min(k1 - 1, lim) : k1 - 1) - (tb + 4 * half);
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * blk + 8 * (i >> 2) + (i & 3) > tlast) s[blk][i] = neg_inf();
+      for (int i = 0; i < 16; ++i)
+        if (8 * (i >> 2) + (i & 3) > tlast) s[i] = neg_inf();
     }
-    float tmax = neg_inf();
+  };
+  // Largest raw score this lane holds of a tile (half of its row's keys).
+  auto lane_max = [&](const f32x16& s) -> float {
+    float t = neg_inf();
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[blk][i]);
-    tmax = max_across_halves(tmax) * a.scale_log2;
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    // P rounded once to the storage dtype. O is normalised by the sum of the
-    // same rounded weights (an exact convex combination of V rows); the LSE
-    // uses the sum of the unrounded weights.
-    u32x4 pk[4];                       // pk[st]: the B operand of 16-token step st
-    float psum = 0.f, pqsum = 0.f;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int blk = st >> 1, hf = st & 1;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x0 = fast_exp2(fmaf(s[blk][8 * hf + 2 * j], a.scale_log2, -m_use));
-        const float x1 = fast_exp2(fmaf(s[blk][8 * hf + 2 * j + 1], a.scale_log2, -m_use));
-        pk[st][j] = T::pack2(x0, x1);
-        pqsum = T::add_pair(pk[st][j], pqsum);
-        psum += x0 + x1;
-      }
-    }
-    l_run = l_run * alpha + psum;
-    lq_run = lq_run * alpha + pqsum;
-    // Rescale only when some row's running max moved (wave-uniform branch).
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+    for (int i = 0; i < 16; ++i) t = fmaxf(t, s[i]);
+    return t;
+  };
+  // Moves the reference where some lane's scores outgrew the threshold
+  // (wave-uniform branch): every row takes its full maximum over both halves,
+  // and O and the sum are rescaled by the same factor.
+  auto maybe_rescale = [&](float lmax) {
+    if (__builtin_amdgcn_ballot_w64(lmax > thr) != 0) {
+      const float m_new = fmaxf(m_ref, max_across_halves(lmax) * a.scale_log2);
+      const float alpha = (m_new == neg_inf()) ? 1.f : fast_exp2(m_ref - m_new);
+      m_ref = m_new;
+      neg_m = (m_new == neg_inf()) ? 0.f : -m_new;
+      thr = (m_new == neg_inf()) ? neg_inf() : (m_new + kRescaleSlack) * inv_scale_log2;
+      l_run *= alpha;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) acc[mb] *= alpha;
     }
-
-    // O^T += V^T P^T over four 16-token steps. Step st covers tokens
-    // 16st + 4*half + {0..3} (first read) and + {8..11} (second read), the
-    // order in which pk[st] holds them.
+  };
+  // Weights of a tile, rounded to the storage dtype: pk[st] is the B operand
+  // of 16-token step st of the PV product.
+  auto weights = [&](const f32x16& s, u32x4 (&pk)[2]) {
+    float sum = l_run;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int r0 = 16 * st + 4 * half + vq;
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x0 = fast_exp2(fmaf(s[8 * st + 2 * j], a.scale_log2, neg_m));
+        const float x1 = fast_exp2(fmaf(s[8 * st + 2 * j + 1], a.scale_log2, neg_m));
+        pk[st][j] = T::pack2(x0, x1);
+        sum = T::add_pair(pk[st][j], sum);
+      }
+    }
+    l_run = sum;
+  };
+  // O^T += V^T P^T over two 16-token steps. Step st covers tokens
+  // 16st + 4*half + {0..3} (first read) and + {8..11} (second read), the
+  // order in which pk[st] holds them.
+  auto pv = [&](const char* vt, const u32x4 (&pk)[2]) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        const int c = 4 * mb + vchunk_lo;
-        const s16x4 lo = lds_read_tr16_b64(vt + v_at(r0, c) + vbyte);
-        const s16x4 hi = lds_read_tr16_b64(vt + v_at(r0 + 8, c) + vbyte);
+        const char* p = vt + 4096 * st + va[mb];
+        const s16x4 lo = lds_read_tr16_b64(p);
+        const s16x4 hi = lds_read_tr16_b64(p + 8 * kRowBytes);
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
         acc[mb] = T::mfma_32x32x16(u32x4{l2[0], l2[1], h2[0], h2[1]}, pk[st], acc[mb]);
       }
     }
-
-    wait_lds_loads();
-    __syncthreads();
   };
-  for (int ti = 0; ti < ntiles; ti += 2) {
-    step(ti, sKa, sVa, sKb, sVb);
-    if (ti + 1 < ntiles) step(ti + 1, sKb, sVb, sKa, sVa);
+
+  // The two halves of a pipelined iteration. The instruction order is written
+  // out: each step issues an LDS read two MFMAs ahead of its use, one MFMA,
+  // and a slice of the VALU work of the other tile, and a scheduling fence
+  // (sched_barrier) keeps the compiler from regrouping the steps.
+  auto k_read = [&](const char* kt, int kk) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(kt + ka[kk]);
+  };
+  auto v_read = [&](const char* vt, int i) -> u32x4 {   // step i = (st, mb) = (i/4, i%4)
+    const char* p = vt + 4096 * (i >> 2) + va[i & 3];
+    const u32x2 lo = __builtin_bit_cast(u32x2, lds_read_tr16_b64(p));
+    const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16_b64(p + 8 * kRowBytes));
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+  // S(j+1) (8 MFMAs over d) with the weights of tile j, one pair of scores
+  // per MFMA; kf[0..1] hold the first two K operands on entry. The last two
+  // steps read the first two V operands of the PV product into vf[0..1].
+  auto qk_weights = [&](const char* kt, u32x4 (&kf)[3], f32x16& s, const f32x16& sc,
+                        u32x4 (&pk)[2], const char* vt, u32x4 (&vf)[3]) {
+    float sum = l_run;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      if (kk + 2 < 8) kf[(kk + 2) % 3] = k_read(kt, kk + 2);
+      else vf[kk - 6] = v_read(vt, kk - 6);
+      s = T::mfma_32x32x16(kf[kk % 3], qv[kk], kk == 0 ? f32x16{} : s);
+      const float x0 = fast_exp2(fmaf(sc[2 * kk], a.scale_log2, neg_m));
+      const float x1 = fast_exp2(fmaf(sc[2 * kk + 1], a.scale_log2, neg_m));
+      pk[kk >> 2][kk & 3] = T::pack2(x0, x1);
+      sum = T::add_pair(pk[kk >> 2][kk & 3], sum);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run = sum;
+  };
+  // PV of tile j (8 MFMAs) with the lane maxima of tile j+1's scores, one
+  // pair per MFMA; returns the lane maximum (raw scores).
+  auto pv_max = [&](const char* vt, u32x4 (&vf)[3], const u32x4 (&pk)[2],
+                    const f32x16& sn) -> float {
+    float t = neg_inf();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i + 2 < 8) vf[(i + 2) % 3] = v_read(vt, i + 2);
+      acc[i & 3] = T::mfma_32x32x16(vf[i % 3], pk[i >> 2], acc[i & 3]);
+      t = fmaxf(fmaxf(t, sn[2 * i]), sn[2 * i + 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return t;
+  };
+
+  // Software pipeline over KV tiles. Iteration j: the loads of K(j+4) and
+  // V(j+3) are issued; the MFMA units compute S(j+1) while the VALU forms the
+  // weights of tile j; then the PV product of tile j runs while the VALU takes
+  // tile j+1's row maxima. The iteration ends by waiting for the loads of
+  // K(j+2) and V(j+1) (issued two iterations earlier; the last two
+  // iterations' loads stay in flight) and one barrier. A buffer is refilled
+  // only in the iteration after the barrier that follows its last read.
+  // Every iteration issues the same loads (tiles past the item read zero, or
+  // repeat the last token in generic mode), so the wait counts are constants.
+  constexpr int kLoadsPerIter = MODE == kPagedUniform ? 5 : 6;
+  // Page ids of the K loads of tiles j+4 and j+5 and of the V load of tile j+3.
+  Pids pid_k0, pid_k1, pid_v;
+  Group grp_v{0, 0};   // uniform mode: where the V load of tile j+3 reads
+  // `ph` is j % 4 as a compile-time constant, so buffer choices are constants.
+  auto body = [&](int j, auto ph, f32x16& s_cur, f32x16& s_nxt, bool has_next) {
+    constexpr int p = decltype(ph)::value;
+    char* kn = kbuf(std::integral_constant<int, p>{});                  // receives K(j+4)
+    char* vn = vbuf(std::integral_constant<int, (p + 3) & 3>{});        // receives V(j+3)
+    const char* kt = kbuf(std::integral_constant<int, (p + 1) & 3>{});  // holds K(j+1)
+    const char* vt = vbuf(std::integral_constant<int, p>{});            // holds V(j)
+    u32x4 kf[3], vf[3];
+    if (has_next) {   // the first K operands land while the loads below are issued
+      kf[0] = k_read(kt, 0);
+      kf[1] = k_read(kt, 1);
+    }
+    const Pids pnn = fetch_pids(j + 6);
+    if constexpr (MODE == kPagedUniform) {
+      const Group gk = group_of(j + 4, pid_k0);
+      issue_group(gk, kbase, kn, true);
+      issue_group(grp_v, vbase, vn, false);
+      grp_v = gk;
+    } else {
+      issue(j + 4, pid_k0, kbase, kn, true);
+      issue(j + 3, pid_v, vbase, vn, false);
+      pid_v = pid_k0;
+    }
+    pid_k0 = pid_k1;
+    pid_k1 = pnn;
+
+    u32x4 pk[2];
+    if (has_next) {
+      qk_weights(kt, kf, s_nxt, s_cur, pk, vt, vf);
+      // The weights are complete here (kept from sinking past the branch).
+      asm volatile("" ::"v"(pk[0]), "v"(pk[1]));
+      mask(j + 1, s_nxt);
+      maybe_rescale(pv_max(vt, vf, pk, s_nxt));
+    } else {
+      weights(s_cur, pk);
+      pv(vt, pk);
+    }
+    wait_vm<2 * kLoadsPerIter>();
+    lds_barrier();
+  };
+
+  if (ntiles > 0) {
+    const Pids p0 = fetch_pids(0), p1 = fetch_pids(1), p2 = fetch_pids(2), p3 = fetch_pids(3);
+    pid_k0 = fetch_pids(4);
+    pid_k1 = fetch_pids(5);
+    issue(0, p0, kbase, sK0, true);
+    issue(0, p0, vbase, sV0, false);
+    issue(1, p1, kbase, sK1, true);
+    issue(2, p2, kbase, sK2, true);
+    issue(1, p1, vbase, sV1, false);
+    issue(3, p3, kbase, sK3, true);
+    issue(2, p2, vbase, sV2, false);
+    pid_v = p3;
+    if constexpr (MODE == kPagedUniform) grp_v = group_of(3, p3);
+    // K(0), V(0) and K(1) have landed; K(2), V(1), K(3), V(2) may still be
+    // in flight.
+    wait_vm<8>();
+    lds_barrier();
+
+    f32x16 sA, sB;
+    qk(sK0, sA);
+    mask(0, sA);
+    maybe_rescale(lane_max(sA));
+    // Every wave has read K(0) before iteration 0 refills its buffer.
+    lds_barrier();
+    constexpr std::integral_constant<int, 0> ph0{};
+    constexpr std::integral_constant<int, 1> ph1{};
+    constexpr std::integral_constant<int, 2> ph2{};
+    constexpr std::integral_constant<int, 3> ph3{};
+    int j = 0;
+    for (; j + 4 < ntiles; j += 4) {   // four tiles, each with a successor
+      body(j, ph0, sA, sB, true);
+      body(j + 1, ph1, sB, sA, true);
+      body(j + 2, ph2, sA, sB, true);
+      body(j + 3, ph3, sB, sA, true);
+    }
+    // The last one to four tiles.
+    body(j, ph0, sA, sB, j + 1 < ntiles);
+    if (j + 1 < ntiles) {
+      body(j + 1, ph1, sB, sA, j + 2 < ntiles);
+      if (j + 2 < ntiles) {
+        body(j + 2, ph2, sA, sB, j + 3 < ntiles);
+        if (j + 3 < ntiles) body(j + 3, ph3, sB, sA, false);
+      }
+    }
   }
 
   // Finalize row lr.
   const float l_tot = sum_across_halves(l_run);
-  const float lq_tot = sum_across_halves(lq_run);
   if (!row_ok) return;
-  const float inv = lq_tot > 0.f ? 1.f / lq_tot : 0.f;
-  const float lse = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : neg_inf();
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse = l_tot > 0.f ? (m_ref + fast_log2(l_tot)) * kLn2 : neg_inf();
   if (slot < 0) {
     const int64_t orow = static_cast<int64_t>(q0 + qtok) * a.num_qo_heads + head;
     OUT* o = static_cast<OUT*>(a.o) + orow * D;
@@ -360,6 +568,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
 
 template <class T, class OUT>
 hipError_t launch_prefill_t(const PrefillArgs& a, PageMode mode, int32_t grid, hipStream_t s) {
+  // The uniform kernel locates pages with shifts: other page sizes use the
+  // per-token lookups of the generic kernel.
+  if (mode == kPagedUniform && (a.page_size & (a.page_size - 1)) != 0) mode = kPagedGeneric;
   if (mode == kPagedUniform)
     hipLaunchKernelGGL((prefill_kernel<T, OUT, kPagedUniform>), dim3(grid), dim3(256), 0, s, a);
   else
