@@ -120,6 +120,16 @@ class Runner:
             a = np.asarray(a, np.int32)
             return torch.from_numpy(a if a.size else np.zeros(1, np.int32)).to("cuda")
 
+        if w.kind == "append":
+            self.ak, self.av = dev(w.append_k), dev(w.append_v)
+            self.k, self.v = dev(w.kv.k_cache), dev(w.kv.v_cache)
+            bi, pos = pkv.pkv_append_positions(w.append_indptr, w.kv.kv_indptr,
+                                               w.kv.last_page_len, w.kv.page_size)
+            self.bi, self.pos = dev_i32(bi), dev_i32(pos)
+            self.kv_indptr, self.kv_indices = dev_i32(w.kv.kv_indptr), dev_i32(w.kv.kv_indices)
+            self.lpl = dev_i32(w.kv.last_page_len)
+            self.plan_us = 0.0
+            return
         self.q = dev(w.q)
         self.ws = pkv.Workspace()
         if w.kind == "single_decode":
@@ -170,7 +180,10 @@ class Runner:
         """One run; `attention_done` (decode / prefill) is recorded after the attention
         kernel, before the merge of split chunks."""
         p, w = self.pkv, self.w
-        if w.kind == "single_decode":
+        if w.kind == "append":
+            p.pkv_append_paged_kv(self.ak, self.av, self.bi, self.pos, self.k, self.v,
+                                  self.kv_indptr, self.kv_indices, self.lpl)
+        elif w.kind == "single_decode":
             p.pkv_single_decode(self.q, self.k, self.v, w.sm_scale, float_ws=self.fws, o=self.o,
                                 lse=self.lse)
         elif w.kind == "decode":
@@ -188,6 +201,11 @@ class Runner:
     def work(self):
         """(algorithmic bytes, algorithmic flops, tokens) of one step."""
         w = self.w
+        if w.kind == "append":
+            nnz = w.append_k.shape[0]
+            row = w.append_k.shape[1] * w.append_k.shape[2] * 2      # bytes of one K (or V) row
+            # K and V rows read once and written once, plus the two int32 index arrays
+            return 4 * nnz * row + 8 * nnz, 0.0, nnz
         if w.kind == "single_decode":
             L = w.k.shape[0]
             b = decode_bytes([L], w.num_kv_heads, w.head_dim, 2, 1, w.num_qo_heads)
@@ -241,8 +259,10 @@ def time_steps(torch, runner, steps, warmup, flush):
             float(np.mean(kern)) if kern else None, wall)
 
 
-def cpu_baseline(w, budget_s=15.0):
-    """The oracle as it stands on the host cores, on a bounded sample of requests."""
+def cpu_baseline(w, min_s=10.0, max_s=30.0):
+    """The oracle as it stands on the host cores: whole passes over the same batch, one
+    request at a time, until at least `min_s` seconds of CPU work (stopping early, mid-pass,
+    at `max_s`)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -252,21 +272,26 @@ def cpu_baseline(w, budget_s=15.0):
     kv = w.kv
     t0 = time.perf_counter()
     done = []
-    for b in range(len(kv.kv_lens)):
-        oracle.batch_decode(w.q, kv.k_cache, kv.v_cache, kv.kv_indptr, kv.kv_indices,
-                            kv.last_page_len, w.dtype, w.sm_scale, requests=[b])
-        done.append(b)
-        if time.perf_counter() - t0 > budget_s:
+    passes = 0
+    while time.perf_counter() - t0 < min_s:
+        for b in range(len(kv.kv_lens)):
+            oracle.batch_decode(w.q, kv.k_cache, kv.v_cache, kv.kv_indptr, kv.kv_indices,
+                                kv.last_page_len, w.dtype, w.sm_scale, requests=[b])
+            done.append(b)
+            if time.perf_counter() - t0 > max_s:
+                break
+        passes += 1
+        if time.perf_counter() - t0 > max_s:
             break
     dt = time.perf_counter() - t0
     nbytes = decode_bytes(kv.kv_lens[done], w.num_kv_heads, w.head_dim, 2, len(done),
                           w.num_qo_heads)
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"fp64 NumPy oracle over requests 0..{len(done) - 1} of the same batch "
-                      f"({len(done)} of {len(kv.kv_lens)} requests, all heads) in {dt:.1f} s"}
+            "sample": f"fp64 NumPy oracle, {len(done)} request evaluations ({passes} pass(es) over "
+                      f"the {len(kv.kv_lens)} requests of the same batch, all heads) in {dt:.1f} s"}
 
 
-WORKLOADS = {"single": 0, "decode": 1, "prefill": 2, "cascade": 3, "long": 4}
+WORKLOADS = {"single": 0, "decode": 1, "prefill": 2, "cascade": 3, "long": 4, "append": 5}
 
 
 def main():
@@ -290,12 +315,12 @@ def main():
 
     log(f"[bench] generating workload {args.workload}")
     flush = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
-    names = [args.workload] + ([n for n in ("single", "decode", "prefill", "cascade", "long")
-                                if n != args.workload] if args.all else [])
+    names = [args.workload] + ([n for n in ("single", "decode", "prefill", "cascade", "long",
+                                            "append") if n != args.workload] if args.all else [])
     results = {}
     headline = None
     for name in names:
-        w = wl.FULL[WORKLOADS[name]]()
+        w = wl.append_kv() if name == "append" else wl.FULL[WORKLOADS[name]]()
         r = Runner(name, w, pkv, torch)
         log(f"[bench] {name}: planned in {r.plan_us:.0f} us; timing {args.steps} steps")
         mean_ms, med_ms, kern_ms, wall = time_steps(torch, r, args.steps, args.warmup, flush)
@@ -340,6 +365,8 @@ def main():
             "cascade": "cascade, 128 requests, 8192-token shared prefix, suffix U[64,1024], "
                        "32/8 heads, P=16, fp16",
             "long": "long-context split-KV decode, 4 x 131072 tokens, 64/8 heads, P=64, bf16",
+            "append": "append of the prefill workload's 10420 new tokens' K/V into the paged "
+                      "cache, 8 KV heads, P=16, bf16",
         }[name], "head_dim": 128, "tokens_per_step": r.work()[2],
             "tokens_per_s": res["tokens_per_s"], "plan_us": res["plan_us"]},
         # the dominant kernel (the attention kernel, timed alone with events)

@@ -314,6 +314,44 @@ pkv_status pkv_cascade_run(const pkv_plan_info* plan, const void* q, const pkv_p
                            const int32_t* suffix_indices_d, float sm_scale, void* o, float* lse,
                            void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Appending new K/V rows into a paged cache (docs index "flashinfer.page" >
+ * "Append new K/V tensors to Paged KV-Cache"; the page walk is the one of the
+ * FlashInfer article, section "Block-sparse cache representation").
+ *
+ * The page table (kv_indptr, kv_indices, last_page_len, device arrays, int32)
+ * already describes the cache *after* the append. Appended row n (n < nnz)
+ * names its request b = batch_indices_d[n] and its position t = positions_d[n]
+ * within that request; its K row append_k[n] and V row append_v[n] (each
+ * [num_kv_heads, 128], contiguous, rows num_kv_heads*128 elements apart) are
+ * written to page kv_indices[kv_indptr[b] + t / P], slot t % P, for every KV
+ * head, of k_cache and v_cache. Those pools have the NHD layout `layout`
+ * describes (its k and v fields are not used). Nothing else is written.
+ * A row whose b is outside [0, batch), whose t is outside [0, L_b), or whose
+ * page index t / P is not below the request's page count is skipped. Page ids
+ * are not range-checked on the device (as for the attention runs).
+ * Asynchronous on `stream`; no allocation; element copies are bit-exact.
+ * Errors: PKV_ERR_INVALID_ARG for NULL pointers with nnz > 0, nnz or batch
+ * < 0, misaligned (16-byte) pointers, bad strides (as pkv_paged_kv);
+ * PKV_ERR_UNSUPPORTED for head_dim != 128 or num_kv_heads > 32. */
+pkv_status pkv_append_paged_kv(const void* append_k, const void* append_v, int32_t nnz,
+                               const int32_t* batch_indices_d, const int32_t* positions_d,
+                               void* k_cache, void* v_cache, const pkv_paged_kv* layout,
+                               const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
+                               const int32_t* last_page_len_d, int32_t batch, void* stream);
+
+/* Host helper for the usual case: request b appends A_b = append_indptr_h[b+1]
+ * - append_indptr_h[b] new tokens at the end of its KV (which the page table,
+ * after the append, gives as L_b tokens). Fills, for n = append_indptr_h[b] +
+ * i, batch_indices_h[n] = b and positions_h[n] = L_b - A_b + i; the output
+ * arrays hold append_indptr_h[batch] entries. Host arrays only, no GPU.
+ * Errors: PKV_ERR_INVALID_ARG for a page table that pkv_decode_plan would
+ * reject, a non-monotone append_indptr_h or append_indptr_h[0] != 0, or
+ * A_b > L_b for some b. */
+pkv_status pkv_append_positions(const int32_t* append_indptr_h, const int32_t* kv_indptr_h,
+                                const int32_t* last_page_len_h, int32_t batch, int32_t page_size,
+                                int32_t* batch_indices_h, int32_t* positions_h);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,6 +20,8 @@ docs.flashinfer.ai index "Welcome to FlashInfer's documentation!"):
   article "FlashInfer", section "Block-sparse cache representation";
 * the host-side plan that splits the KV into work chunks:
   article "FlashInfer", section "Plan and run".
+* appending new K/V rows into the paged cache: docs index "flashinfer.page" >
+  "Append new K/V tensors to Paged KV-Cache", with the page walk above.
 
 Every function is pinned by tests under ``tests/`` (brute force on tiny inputs,
 closed forms, invariants, hand-worked golden fixtures). No function here is
@@ -41,3 +43,4 @@ from .attention import (  # noqa: F401
     cascade_decode,
 )
 from .plan import plan_spec, PlanSpec  # noqa: F401
+from .append import append_positions, append_paged_kv  # noqa: F401

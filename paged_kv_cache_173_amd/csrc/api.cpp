@@ -808,4 +808,83 @@ pkv_status pkv_cascade_run(const pkv_plan_info* plan, const void* q, const pkv_p
   return ok();
 }
 
+pkv_status pkv_append_paged_kv(const void* append_k, const void* append_v, int32_t nnz,
+                               const int32_t* batch_indices_d, const int32_t* positions_d,
+                               void* k_cache, void* v_cache, const pkv_paged_kv* layout,
+                               const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
+                               const int32_t* last_page_len_d, int32_t batch, void* stream) {
+  if (layout == nullptr) return fail(PKV_ERR_INVALID_ARG, "layout is NULL");
+  if (nnz < 0 || batch < 0) return fail(PKV_ERR_INVALID_ARG, "nnz and batch must be >= 0");
+  if (layout->page_size <= 0) return fail(PKV_ERR_INVALID_ARG, "page_size must be positive");
+  if (layout->num_kv_heads <= 0) return fail(PKV_ERR_INVALID_ARG, "num_kv_heads must be positive");
+  pkv_status st;
+  if ((st = check_head_dim_dtype(layout->head_dim, layout->dtype))) return st;
+  if (layout->num_kv_heads > 32)
+    return fail(PKV_ERR_UNSUPPORTED, "append supports num_kv_heads <= 32");
+  if (layout->page_stride % 8 || layout->token_stride % 8 || layout->head_stride % 8 ||
+      layout->page_stride < 0 || layout->token_stride < 0 || layout->head_stride < 0 ||
+      layout->page_stride >= (int64_t{1} << 30) || layout->token_stride > (INT32_MAX / 32))
+    return fail(PKV_ERR_INVALID_ARG,
+                "KV strides must be non-negative multiples of 8 elements (page_stride < 2^30, "
+                "token_stride < 2^26)");
+  if (nnz == 0) return ok();
+  if (!append_k || !append_v || !batch_indices_d || !positions_d || !k_cache || !v_cache ||
+      (batch > 0 && (!kv_indptr_d || !kv_indices_d || !last_page_len_d)))
+    return fail(PKV_ERR_INVALID_ARG, "append / cache / page-table pointers must be non-NULL");
+  if (!aligned16(append_k) || !aligned16(append_v) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_ERR_INVALID_ARG, "append_k / append_v / k_cache / v_cache must be 16-byte aligned");
+  if (batch == 0) return ok();   // no request: every row is skipped
+  pkv::AppendArgs a{};
+  a.append_k = append_k;
+  a.append_v = append_v;
+  a.append_stride = static_cast<int64_t>(layout->num_kv_heads) * layout->head_dim;
+  a.batch_indices = batch_indices_d;
+  a.positions = positions_d;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.page_stride = layout->page_stride;
+  a.token_stride = layout->token_stride;
+  a.head_stride = layout->head_stride;
+  a.kv_indptr = kv_indptr_d;
+  a.kv_indices = kv_indices_d;
+  a.last_page_len = last_page_len_d;
+  a.batch = batch;
+  a.page_size = layout->page_size;
+  a.num_kv_heads = layout->num_kv_heads;
+  a.nnz = nnz;
+  hipError_t e = pkv::launch_append(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append kernel launch");
+  return ok();
+}
+
+pkv_status pkv_append_positions(const int32_t* append_indptr_h, const int32_t* kv_indptr_h,
+                                const int32_t* last_page_len_h, int32_t batch, int32_t page_size,
+                                int32_t* batch_indices_h, int32_t* positions_h) {
+  std::vector<int64_t> kv_lens;
+  pkv_status st;
+  if ((st = check_page_table(kv_indptr_h, last_page_len_h, batch, page_size, &kv_lens))) return st;
+  if (append_indptr_h == nullptr) return fail(PKV_ERR_INVALID_ARG, "append_indptr_h is NULL");
+  if (append_indptr_h[0] != 0) return fail(PKV_ERR_INVALID_ARG, "append_indptr_h[0] must be 0");
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t n = static_cast<int64_t>(append_indptr_h[b + 1]) - append_indptr_h[b];
+    if (n < 0)
+      return fail(PKV_ERR_INVALID_ARG, "append_indptr_h is not monotone at " + std::to_string(b));
+    if (n > kv_lens[b])
+      return fail(PKV_ERR_INVALID_ARG, "request " + std::to_string(b) +
+                                           " appends more tokens than its KV length");
+  }
+  if (append_indptr_h[batch] > 0 && (batch_indices_h == nullptr || positions_h == nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "batch_indices_h / positions_h are NULL");
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t first = append_indptr_h[b];
+    const int32_t count = append_indptr_h[b + 1] - first;
+    const int64_t start = kv_lens[b] - count;
+    for (int32_t i = 0; i < count; ++i) {
+      batch_indices_h[first + i] = b;
+      positions_h[first + i] = static_cast<int32_t>(start + i);
+    }
+  }
+  return ok();
+}
+
 }  // extern "C"

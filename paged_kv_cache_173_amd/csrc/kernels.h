@@ -59,6 +59,24 @@ struct PrefillArgs {
   float* part_lse;            // [slot][128 rows]
 };
 
+struct AppendArgs {
+  const void* append_k;       // [nnz] rows of [Hkv, 128], 2-byte elements
+  const void* append_v;
+  int64_t append_stride;      // elements between consecutive appended rows
+  const int32_t* batch_indices;   // device [nnz]
+  const int32_t* positions;       // device [nnz]
+  void* k;                    // K page pool base (written)
+  void* v;                    // V page pool base (written)
+  int64_t page_stride, token_stride, head_stride;  // elements
+  const int32_t* kv_indptr;   // device [batch+1]
+  const int32_t* kv_indices;  // device page ids
+  const int32_t* last_page_len;   // device [batch]
+  int32_t batch;
+  int32_t page_size;
+  int32_t num_kv_heads;       // <= 32
+  int64_t nnz;
+};
+
 struct MergeGroupsArgs {
   const int32_t* groups;      // device [num_groups][8], or NULL: implicit (single decode)
   int32_t implicit_nchunks;
@@ -85,6 +103,8 @@ hipError_t launch_prefill(const PrefillArgs& a, int32_t storage_dtype, OutKind o
 
 hipError_t launch_merge_groups(const MergeGroupsArgs& a, int32_t storage_dtype, OutKind out,
                                int32_t num_groups, hipStream_t stream);
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 
 // Public merges: v dtype in {F16, BF16, F32}; rows = n * H.
 hipError_t launch_merge2(const void* va, const float* sa, const void* vb, const float* sb,

@@ -115,6 +115,11 @@ _lib_merge_state_in_place = _sig("pkv_merge_state_in_place", _I32,
                                  [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P])
 _lib_merge_states = _sig("pkv_merge_states", _I32,
                          [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P])
+_lib_append_paged_kv = _sig("pkv_append_paged_kv", _I32,
+                            [_P, _P, _I32, _P, _P, _P, _P, ctypes.POINTER(pkv_paged_kv), _P, _P,
+                             _P, _I32, _P])
+_lib_append_positions = _sig("pkv_append_positions", _I32,
+                             [_I32P, _I32P, _I32P, _I32, _I32, _I32P, _I32P])
 _lib_cascade_plan = _sig("pkv_cascade_plan", _I32,
                          [_I32, _I32, _I32P, _I32P, _I32, _I32, _I32, _I32, _I32, _I32,
                           ctypes.POINTER(pkv_sched), _P, _SZ, _P, _SZ, _P, _SZ, _P,
@@ -456,6 +461,48 @@ def pkv_cascade_run(plan: pkv_plan_info, q, k_cache, v_cache, prefix_indices_d, 
                             suffix_indices_d.data_ptr(), float(sm_scale), o.data_ptr(), _ptr(lse),
                             _stream(stream)), "pkv_cascade_run")
     return o, lse
+
+
+def pkv_append_paged_kv(append_k, append_v, batch_indices_d, positions_d, k_cache, v_cache,
+                        kv_indptr_d, kv_indices_d, last_page_len_d, stream=None):
+    """Write appended rows append_k / append_v [nnz, Hkv, D] into the NHD pools k_cache /
+    v_cache (in place) at the (request, position) each row names."""
+    if append_k.shape != append_v.shape or append_k.dim() != 3:
+        raise ValueError("append_k and append_v must both be [nnz, num_kv_heads, head_dim]")
+    if append_k.dtype != k_cache.dtype or append_v.dtype != v_cache.dtype:
+        raise ValueError("appended rows must have the cache's dtype")
+    append_k, append_v = append_k.contiguous(), append_v.contiguous()
+    layout = paged_kv(k_cache, v_cache)
+    if append_k.shape[1] != layout.num_kv_heads or append_k.shape[2] != layout.head_dim:
+        raise ValueError("appended rows must be [nnz, num_kv_heads, head_dim] of the cache")
+    for name, t in (("batch_indices_d", batch_indices_d), ("positions_d", positions_d),
+                    ("kv_indptr_d", kv_indptr_d), ("kv_indices_d", kv_indices_d),
+                    ("last_page_len_d", last_page_len_d)):
+        if t.dtype != torch.int32:
+            raise TypeError(f"{name} must be int32")
+        _device_tensor(t, name)
+    nnz = append_k.shape[0]
+    if batch_indices_d.numel() < nnz or positions_d.numel() < nnz:
+        raise ValueError("batch_indices_d / positions_d need one entry per appended row")
+    _check(_lib_append_paged_kv(append_k.data_ptr(), append_v.data_ptr(), nnz,
+                                batch_indices_d.data_ptr(), positions_d.data_ptr(),
+                                k_cache.data_ptr(), v_cache.data_ptr(), ctypes.byref(layout),
+                                kv_indptr_d.data_ptr(), kv_indices_d.data_ptr(),
+                                last_page_len_d.data_ptr(), kv_indptr_d.numel() - 1,
+                                _stream(stream)), "pkv_append_paged_kv")
+    return k_cache, v_cache
+
+
+def pkv_append_positions(append_indptr, kv_indptr, last_page_len, page_size):
+    """(batch_indices, positions) int32 arrays for requests that append their new tokens at
+    the end of their KV (host arrays; the page table describes the cache after the append)."""
+    aip, kip, lpl = _host_i32(append_indptr), _host_i32(kv_indptr), _host_i32(last_page_len)
+    nnz = int(aip[-1]) if aip.size else 0
+    bi = np.zeros(max(nnz, 1), dtype=np.int32)
+    pos = np.zeros(max(nnz, 1), dtype=np.int32)
+    _check(_lib_append_positions(_i32p(aip), _i32p(kip), _i32p(lpl), len(kip) - 1, int(page_size),
+                                 _i32p(bi), _i32p(pos)), "pkv_append_positions")
+    return bi[:nnz], pos[:nnz]
 
 
 def read_plan_tables(plan: pkv_plan_info, workspace: Workspace, part: int = 0):

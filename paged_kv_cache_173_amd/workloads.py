@@ -248,6 +248,56 @@ def long_decode(seed=173004, batch=4, kv_len=131072, num_qo_heads=64, num_kv_hea
     return w
 
 
+@dataclass
+class AppendWorkload:
+    """New K/V rows to write into a paged cache whose page table already covers them."""
+    kind = "append"              # (class attribute, not a field)
+    dtype: str
+    kv: PagedKV                  # page table after the append; pools as they are before it
+    append_k: np.ndarray         # [nnz, Hkv, D] bit patterns
+    append_v: np.ndarray
+    append_indptr: np.ndarray    # int32 [B+1]: request b appends rows append_indptr[b]..[b+1]-1
+    meta: dict = field(default_factory=dict)
+
+
+def append_kv(seed=173002, batch=16, new_min=128, new_max=1024, prefix_min=0, prefix_max=2048,
+              num_kv_heads=8, head_dim=128, page_size=16, dtype="bf16", canary=False,
+              new_lens=None, prefix_lens=None):
+    """The K/V of a prefill step's new tokens, appended after each request's cached prefix.
+
+    With the default seed the lengths are those of the causal prefill workload
+    (new tokens = its query tokens; same draws, same order). Draw order:
+    new lengths, prefix lengths, pool permutation, K pool, V pool, appended K
+    rows, appended V rows. With ``canary`` the unused pool pages, the slots past
+    each last_page_len and the slots the append will write hold NaN.
+    """
+    rng = np.random.default_rng(seed)
+    if new_lens is None:
+        new_lens = rng.integers(new_min, new_max + 1, size=batch)
+    if prefix_lens is None:
+        prefix_lens = rng.integers(prefix_min, prefix_max + 1, size=len(new_lens))
+    new_lens = np.asarray(new_lens, dtype=np.int64)
+    prefix_lens = np.asarray(prefix_lens, dtype=np.int64)
+    kv_lens = new_lens + prefix_lens
+    kv, _, _ = make_paged(rng, kv_lens, page_size, num_kv_heads, head_dim, dtype,
+                          (0, num_kv_heads, head_dim))
+    nnz = int(new_lens.sum())
+    append_k = normal_bits(rng, (nnz, num_kv_heads, head_dim), dtype)
+    append_v = normal_bits(rng, (nnz, num_kv_heads, head_dim), dtype)
+    append_indptr = np.zeros(len(new_lens) + 1, dtype=np.int32)
+    append_indptr[1:] = np.cumsum(new_lens)
+    if canary:
+        canary_tails(kv, dtype)
+        nan = nan_bits(dtype)
+        for b in range(len(kv_lens)):
+            for t in range(int(prefix_lens[b]), int(kv_lens[b])):
+                page = kv.kv_indices[kv.kv_indptr[b] + t // page_size]
+                kv.k_cache[page, t % page_size] = nan
+                kv.v_cache[page, t % page_size] = nan
+    return AppendWorkload(dtype, kv, append_k, append_v, append_indptr,
+                          meta={"seed": seed, "new_lens": new_lens, "prefix_lens": prefix_lens})
+
+
 # Full-size workloads, in the order they are numbered in the tests and bench.
 FULL = {
     0: lambda **kw: single_decode(seed=173000, **kw),

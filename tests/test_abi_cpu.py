@@ -167,3 +167,46 @@ def test_runs_reject_bad_scales(lib):
                                    None, None, None) == lib.PKV_ERR_INVALID_ARG
         assert lib._lib_prefill_run(ctypes.byref(info), None, ctypes.byref(kv), None, None, None,
                                     scale, None, None, None) == lib.PKV_ERR_INVALID_ARG
+
+
+def test_append_validates_before_any_launch(lib):
+    def layout(P=16, H=8, D=128, dtype=0, ps=None, ts=None, hs=128):
+        kv = lib.pkv_paged_kv()
+        kv.page_size, kv.num_kv_heads, kv.head_dim, kv.dtype = P, H, D, dtype
+        kv.token_stride = H * D if ts is None else ts
+        kv.page_stride = P * kv.token_stride if ps is None else ps
+        kv.head_stride = hs
+        return kv
+
+    def call(kv, nnz=4, ptr=16, batch=2):
+        return lib._lib_append_paged_kv(ptr, ptr, nnz, ptr, ptr, ptr, ptr, ctypes.byref(kv),
+                                        ptr, ptr, ptr, batch, None)
+
+    assert lib._lib_append_paged_kv(None, None, 1, None, None, None, None, None, None, None,
+                                    None, 1, None) == lib.PKV_ERR_INVALID_ARG   # NULL layout
+    assert call(layout(), nnz=-1) == lib.PKV_ERR_INVALID_ARG
+    assert call(layout(), batch=-1) == lib.PKV_ERR_INVALID_ARG
+    assert call(layout(D=64)) == lib.PKV_ERR_UNSUPPORTED
+    assert call(layout(H=33)) == lib.PKV_ERR_UNSUPPORTED
+    assert call(layout(dtype=2)) == lib.PKV_ERR_UNSUPPORTED
+    assert call(layout(P=0)) == lib.PKV_ERR_INVALID_ARG
+    assert call(layout(hs=4)) == lib.PKV_ERR_INVALID_ARG                   # stride not a multiple of 8
+    assert call(layout(ps=1 << 30)) == lib.PKV_ERR_INVALID_ARG             # page stride too large
+    assert call(layout(), ptr=8) == lib.PKV_ERR_INVALID_ARG                # misaligned pointers
+    kv = layout()
+    assert lib._lib_append_paged_kv(None, None, 3, None, None, None, None, ctypes.byref(kv), None,
+                                    None, None, 1, None) == lib.PKV_ERR_INVALID_ARG
+    # nothing to append: no pointer is needed and nothing is launched
+    assert lib._lib_append_paged_kv(None, None, 0, None, None, None, None, ctypes.byref(kv), None,
+                                    None, None, 1, None) == lib.PKV_OK
+
+
+def test_append_positions_host_helper(lib):
+    bi, pos = lib.pkv_append_positions([0, 2, 2, 5], [0, 1, 1, 3], [3, 0, 2], 4)
+    assert bi.tolist() == [0, 0, 2, 2, 2] and pos.tolist() == [1, 2, 3, 4, 5]
+    for args in (([0, 5], [0, 1], [3], 4),         # more rows than the request holds
+                 ([1, 2], [0, 1], [3], 4),         # append_indptr[0] != 0
+                 ([0, 2, 1], [0, 1, 2], [3, 3], 4),  # not monotone
+                 ([0, 1], [0, 1], [5], 4)):        # last_page_len > page_size
+        with pytest.raises(lib.PkvError):
+            lib.pkv_append_positions(*args)
