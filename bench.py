@@ -120,6 +120,18 @@ class Runner:
             a = np.asarray(a, np.int32)
             return torch.from_numpy(a if a.size else np.zeros(1, np.int32)).to("cuda")
 
+        if w.kind == "block_sparse":
+            self.q, self.k, self.v = dev(w.q), dev(w.k), dev(w.v)
+            self.ip, self.ix = dev_i32(w.bsr_indptr), dev_i32(w.bsr_indices)
+            self.ws = pkv.Workspace()
+            self.dt = dt
+            self.o = torch.empty_like(self.q)
+            self.lse = torch.empty(self.q.shape[:2], dtype=torch.float32, device="cuda")
+            self._plan()
+            t0 = time.perf_counter()
+            self._plan()
+            self.plan_us = (time.perf_counter() - t0) * 1e6
+            return
         if w.kind == "append":
             self.ak, self.av = dev(w.append_k), dev(w.append_v)
             self.k, self.v = dev(w.kv.k_cache), dev(w.kv.v_cache)
@@ -154,7 +166,12 @@ class Runner:
 
     def _plan(self):
         w, pkv, torch, dt = self.w, self.pkv, self.torch, self.dt
-        if w.kind == "single_decode":
+        if w.kind == "block_sparse":
+            self.plan = pkv.pkv_block_sparse_plan(w.bsr_indptr, w.bsr_indices, w.q.shape[0],
+                                                  w.k.shape[0], w.row_block, w.col_block,
+                                                  w.num_qo_heads, w.num_kv_heads, w.head_dim, dt,
+                                                  self.ws)
+        elif w.kind == "single_decode":
             need = pkv._I64(0)
             pkv._lib_single_decode(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(),
                                    w.k.shape[0], w.num_qo_heads, w.num_kv_heads, w.head_dim,
@@ -180,7 +197,10 @@ class Runner:
         """One run; `attention_done` (decode / prefill) is recorded after the attention
         kernel, before the merge of split chunks."""
         p, w = self.pkv, self.w
-        if w.kind == "append":
+        if w.kind == "block_sparse":
+            p.pkv_block_sparse_run(self.plan, self.q, self.k, self.v, self.ip, self.ix,
+                                   w.sm_scale, o=self.o, lse=self.lse)
+        elif w.kind == "append":
             p.pkv_append_paged_kv(self.ak, self.av, self.bi, self.pos, self.k, self.v,
                                   self.kv_indptr, self.kv_indices, self.lpl)
         elif w.kind == "single_decode":
@@ -201,6 +221,16 @@ class Runner:
     def work(self):
         """(algorithmic bytes, algorithmic flops, tokens) of one step."""
         w = self.w
+        if w.kind == "block_sparse":
+            R, C, Nq, Nkv = w.row_block, w.col_block, w.q.shape[0], w.k.shape[0]
+            pairs = 0
+            for i in range(len(w.bsr_indptr) - 1):
+                rows = min(R, Nq - i * R)
+                cols = w.bsr_indices[w.bsr_indptr[i]:w.bsr_indptr[i + 1]]
+                pairs += rows * int(np.sum(np.minimum(C, Nkv - cols * C)))
+            f = 4.0 * w.head_dim * w.num_qo_heads * pairs
+            b = w.q.size * 2 * 2 + w.k.size * 2 * 2 + Nq * w.num_qo_heads * 4
+            return b, f, Nq
         if w.kind == "append":
             nnz = w.append_k.shape[0]
             row = w.append_k.shape[1] * w.append_k.shape[2] * 2      # bytes of one K (or V) row
@@ -291,7 +321,8 @@ def cpu_baseline(w, min_s=10.0, max_s=30.0):
                       f"the {len(kv.kv_lens)} requests of the same batch, all heads) in {dt:.1f} s"}
 
 
-WORKLOADS = {"single": 0, "decode": 1, "prefill": 2, "cascade": 3, "long": 4, "append": 5}
+WORKLOADS = {"single": 0, "decode": 1, "prefill": 2, "cascade": 3, "long": 4, "append": 5,
+             "block_sparse": 6}
 
 
 def main():
@@ -316,11 +347,13 @@ def main():
     log(f"[bench] generating workload {args.workload}")
     flush = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
     names = [args.workload] + ([n for n in ("single", "decode", "prefill", "cascade", "long",
-                                            "append") if n != args.workload] if args.all else [])
+                                            "append", "block_sparse")
+                                 if n != args.workload] if args.all else [])
     results = {}
     headline = None
     for name in names:
-        w = wl.append_kv() if name == "append" else wl.FULL[WORKLOADS[name]]()
+        w = (wl.append_kv() if name == "append" else
+             wl.block_sparse() if name == "block_sparse" else wl.FULL[WORKLOADS[name]]())
         r = Runner(name, w, pkv, torch)
         log(f"[bench] {name}: planned in {r.plan_us:.0f} us; timing {args.steps} steps")
         mean_ms, med_ms, kern_ms, wall = time_steps(torch, r, args.steps, args.warmup, flush)
@@ -347,7 +380,7 @@ def main():
             torch.cuda.empty_cache()
 
     name, w, r, res = headline
-    prefill_like = name == "prefill"
+    prefill_like = name in ("prefill", "block_sparse")
     line = {
         "metric": "paged decode HBM GB/s (% peak); prefill TFLOPS (% MFMA peak); tokens/s",
         "value": res["TFLOPs"] if prefill_like else res["GBps"],
@@ -367,6 +400,8 @@ def main():
             "long": "long-context split-KV decode, 4 x 131072 tokens, 64/8 heads, P=64, bf16",
             "append": "append of the prefill workload's 10420 new tokens' K/V into the paged "
                       "cache, 8 KV heads, P=16, bf16",
+            "block_sparse": "block-sparse attention, 8192 x 8192 tokens, 64 x 64 blocks, "
+                            "density 0.25 + diagonal, 32/8 heads, bf16",
         }[name], "head_dim": 128, "tokens_per_step": r.work()[2],
             "tokens_per_s": res["tokens_per_s"], "plan_us": res["plan_us"]},
         # the dominant kernel (the attention kernel, timed alone with events)

@@ -72,7 +72,7 @@ typedef int32_t pkv_dtype;
 enum { PKV_F16 = 0, PKV_BF16 = 1, PKV_F32 = 2 };
 
 typedef int32_t pkv_kind;
-enum { PKV_KIND_DECODE = 1, PKV_KIND_PREFILL = 2, PKV_KIND_CASCADE = 3 };
+enum { PKV_KIND_DECODE = 1, PKV_KIND_PREFILL = 2, PKV_KIND_CASCADE = 3, PKV_KIND_BLOCK_SPARSE = 4 };
 
 /* A paged K/V cache. k and v are separate device bases with one set of
  * strides (in elements), which also covers an interleaved [pages, 2, P, H, D]
@@ -313,6 +313,42 @@ pkv_status pkv_cascade_run(const pkv_plan_info* plan, const void* q, const pkv_p
                            const int32_t* prefix_indices_d, const int32_t* suffix_indptr_d,
                            const int32_t* suffix_indices_d, float sm_scale, void* o, float* lse,
                            void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Block-sparse attention (docs index "flashinfer.sparse" >
+ * "BlockSparseAttentionWrapper"; the block-sparse view of the cache in the
+ * FlashInfer article, section "Block-sparse cache representation"). Queries
+ * q [num_qo_tokens, Hq, 128] and dense keys / values k, v
+ * [num_kv_tokens, Hkv, 128] (contiguous) are cut into blocks of row_block (R)
+ * query tokens and col_block (C) key tokens; the mask is a BSR matrix over
+ * those blocks: block row i (query tokens iR .. min(iR+R, N_q)-1) sees the
+ * key blocks bsr_indices[bsr_indptr[i] .. bsr_indptr[i+1]-1] (strictly
+ * ascending; block j holds keys jC .. min(jC+C, N_kv)-1). Every query token of
+ * a block row attends, unmasked, to every key of its listed blocks; a row with
+ * no block gets O = 0 and LSE = -inf. The output o [num_qo_tokens, Hq, 128]
+ * is in the storage dtype, lse [num_qo_tokens, Hq] float32 natural log (or
+ * NULL). The paged layout is the R = 1 case: a block row is a request of R
+ * query tokens whose pages are its blocks (page_size C over the dense K/V),
+ * so the plan and the kernel are the paged prefill's, unmasked.
+ * plan validates on the host: num_block_rows = ceil(N_q / R), the indptr
+ * monotone from 0, indices ascending within [0, ceil(N_kv / C)); errors as
+ * pkv_prefill_plan, plus PKV_ERR_INVALID_ARG for a bad pattern. The plan keeps
+ * the query-block offsets in int_ws. run takes the device copies of the BSR
+ * arrays (the same values the plan saw).
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_block_sparse_plan(const int32_t* bsr_indptr_h, const int32_t* bsr_indices_h,
+                                 int32_t num_block_rows, int32_t num_qo_tokens,
+                                 int32_t num_kv_tokens, int32_t row_block, int32_t col_block,
+                                 int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 pkv_dtype dtype, const pkv_sched* sched, void* int_ws,
+                                 size_t int_ws_bytes, void* float_ws, size_t float_ws_bytes,
+                                 void* host_ws, size_t host_ws_bytes, void* stream,
+                                 pkv_plan_info* out);
+
+pkv_status pkv_block_sparse_run(const pkv_plan_info* plan, const void* q, const void* k,
+                                const void* v, const int32_t* bsr_indptr_d,
+                                const int32_t* bsr_indices_d, float sm_scale, void* o, float* lse,
+                                void* stream);
 
 /* ---------------------------------------------------------------------------
  * Appending new K/V rows into a paged cache (docs index "flashinfer.page" >

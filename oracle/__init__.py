@@ -22,6 +22,8 @@ docs.flashinfer.ai index "Welcome to FlashInfer's documentation!"):
   article "FlashInfer", section "Plan and run".
 * appending new K/V rows into the paged cache: docs index "flashinfer.page" >
   "Append new K/V tensors to Paged KV-Cache", with the page walk above.
+* block-sparse attention: docs index "flashinfer.sparse" >
+  "BlockSparseAttentionWrapper", with exact attention over a block mask.
 
 Every function is pinned by tests under ``tests/`` (brute force on tiny inputs,
 closed forms, invariants, hand-worked golden fixtures). No function here is
@@ -44,3 +46,4 @@ from .attention import (  # noqa: F401
 )
 from .plan import plan_spec, PlanSpec  # noqa: F401
 from .append import append_positions, append_paged_kv  # noqa: F401
+from .block_sparse import block_mask, block_sparse_attention  # noqa: F401

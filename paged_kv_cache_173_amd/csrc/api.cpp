@@ -808,6 +808,114 @@ pkv_status pkv_cascade_run(const pkv_plan_info* plan, const void* q, const pkv_p
   return ok();
 }
 
+pkv_status pkv_block_sparse_plan(const int32_t* bsr_indptr_h, const int32_t* bsr_indices_h,
+                                 int32_t num_block_rows, int32_t num_qo_tokens,
+                                 int32_t num_kv_tokens, int32_t row_block, int32_t col_block,
+                                 int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 pkv_dtype dtype, const pkv_sched* sched, void* int_ws,
+                                 size_t int_ws_bytes, void* float_ws, size_t float_ws_bytes,
+                                 void* host_ws, size_t host_ws_bytes, void* stream,
+                                 pkv_plan_info* out) {
+  if (out == nullptr) return fail(PKV_ERR_INVALID_ARG, "out is NULL");
+  pkv_status st;
+  if ((st = check_heads(num_qo_heads, num_kv_heads))) return st;
+  if ((st = check_head_dim_dtype(head_dim, dtype))) return st;
+  const int32_t G = num_qo_heads / num_kv_heads;
+  if (G > kRowsPerPrefillTile)
+    return fail(PKV_ERR_UNSUPPORTED, "block-sparse supports num_qo_heads / num_kv_heads <= 128");
+  if (row_block <= 0 || col_block <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "row_block and col_block must be positive");
+  if (num_qo_tokens < 0 || num_kv_tokens < 0)
+    return fail(PKV_ERR_INVALID_ARG, "token counts must be >= 0");
+  if (static_cast<int64_t>(num_qo_tokens) * num_qo_heads > INT32_MAX)
+    return fail(PKV_ERR_INVALID_ARG, "query rows overflow int32");
+  const int64_t want_rows = (static_cast<int64_t>(num_qo_tokens) + row_block - 1) / row_block;
+  if (num_block_rows != want_rows)
+    return fail(PKV_ERR_INVALID_ARG, "num_block_rows must be ceil(num_qo_tokens / row_block)");
+  if (bsr_indptr_h == nullptr || bsr_indptr_h[0] != 0)
+    return fail(PKV_ERR_INVALID_ARG, "bsr_indptr_h must be non-NULL with bsr_indptr_h[0] = 0");
+  const int64_t num_col_blocks = (static_cast<int64_t>(num_kv_tokens) + col_block - 1) / col_block;
+  if (num_col_blocks * col_block * static_cast<int64_t>(num_kv_heads) * head_dim >
+      (int64_t{1} << 40))
+    return fail(PKV_ERR_INVALID_ARG, "keys too large");
+  if (static_cast<int64_t>(col_block) * num_kv_heads * head_dim >= (int64_t{1} << 30))
+    return fail(PKV_ERR_INVALID_ARG, "col_block * num_kv_heads * head_dim must be below 2^30");
+  std::vector<int64_t> qo_lens(num_block_rows), kv_lens(num_block_rows);
+  const int64_t last_block_len = num_kv_tokens - (num_col_blocks - 1) * col_block;
+  for (int32_t i = 0; i < num_block_rows; ++i) {
+    const int32_t b0 = bsr_indptr_h[i], b1 = bsr_indptr_h[i + 1];
+    if (b1 < b0) return fail(PKV_ERR_INVALID_ARG, "bsr_indptr is not monotone at " + std::to_string(i));
+    if (b1 > b0 && bsr_indices_h == nullptr)
+      return fail(PKV_ERR_INVALID_ARG, "bsr_indices_h is NULL");
+    int64_t len = 0;
+    for (int32_t e = b0; e < b1; ++e) {
+      const int32_t j = bsr_indices_h[e];
+      if (j < 0 || j >= num_col_blocks || (e > b0 && j <= bsr_indices_h[e - 1]))
+        return fail(PKV_ERR_INVALID_ARG, "bsr_indices of block row " + std::to_string(i) +
+                                             " must ascend within [0, ceil(num_kv_tokens / C))");
+      len += (j == num_col_blocks - 1) ? last_block_len : col_block;
+    }
+    qo_lens[i] = std::min<int64_t>(row_block, num_qo_tokens - static_cast<int64_t>(i) * row_block);
+    kv_lens[i] = len;
+  }
+  pkv_sched s;
+  if ((st = resolve_sched(sched, PKV_KIND_PREFILL, &s))) return st;
+  pkv::HostPlan hp;
+  std::string err;
+  if (!pkv::build_plan(make_input(qo_lens, kv_lens, col_block, num_kv_heads, G,
+                                  kRowsPerPrefillTile, false, s),
+                       &hp, &err))
+    return fail(PKV_ERR_INVALID_ARG, err);
+  fill_header(out, PKV_KIND_BLOCK_SPARSE, dtype, num_block_rows, num_qo_heads, num_kv_heads,
+              head_dim, col_block, num_qo_tokens, s);
+  Layout lay;
+  // int ws: the query-block offsets [num_block_rows + 1], then the part's tables
+  lay.int_bytes = align_up((static_cast<int64_t>(num_block_rows) + 1) * 4);
+  place_part(hp, num_block_rows, kRowsPerPrefillTile, 0, &lay, &out->part[0]);
+  if (host_ws != nullptr && host_ws_bytes >= static_cast<size_t>(lay.int_bytes)) {
+    int32_t* qo = static_cast<int32_t*>(host_ws);
+    for (int32_t i = 0; i <= num_block_rows; ++i)
+      qo[i] = static_cast<int32_t>(std::min<int64_t>(static_cast<int64_t>(i) * row_block,
+                                                     num_qo_tokens));
+    write_part(hp, kv_lens, out->part[0], static_cast<char*>(host_ws));
+  }
+  if ((st = commit_plan(lay, int_ws, int_ws_bytes, float_ws, float_ws_bytes, host_ws,
+                        host_ws_bytes, static_cast<hipStream_t>(stream), out)))
+    return st;
+  return ok();
+}
+
+pkv_status pkv_block_sparse_run(const pkv_plan_info* plan, const void* q, const void* k,
+                                const void* v, const int32_t* bsr_indptr_d,
+                                const int32_t* bsr_indices_d, float sm_scale, void* o, float* lse,
+                                void* stream) {
+  pkv_status st;
+  if ((st = check_scale(sm_scale))) return st;
+  if ((st = check_plan(plan, PKV_KIND_BLOCK_SPARSE))) return st;
+  if (plan->total_qo == 0) return ok();
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || bsr_indptr_d == nullptr ||
+      bsr_indices_d == nullptr)
+    return fail(PKV_ERR_INVALID_ARG, "q, k, v, o and the BSR arrays must be non-NULL");
+  if (!aligned16(q) || !aligned16(o) || !aligned16(k) || !aligned16(v))
+    return fail(PKV_ERR_INVALID_ARG, "q / k / v / o must be 16-byte aligned");
+  // The dense keys viewed as pages of col_block tokens: page j = key block j.
+  pkv_paged_kv kv{};
+  kv.k = k;
+  kv.v = v;
+  kv.token_stride = static_cast<int64_t>(plan->num_kv_heads) * plan->head_dim;
+  kv.head_stride = plan->head_dim;
+  kv.page_stride = kv.token_stride * plan->page_size;
+  kv.page_size = plan->page_size;
+  kv.num_kv_heads = plan->num_kv_heads;
+  kv.head_dim = plan->head_dim;
+  kv.dtype = plan->dtype;
+  if ((st = run_prefill_part(plan, plan->part[0], q, &kv, i_at(plan->int_ws, 0), bsr_indptr_d,
+                             bsr_indices_d, sm_scale, o, lse, plan->num_qo_heads,
+                             pkv::kOutStorage, static_cast<hipStream_t>(stream))))
+    return st;
+  return ok();
+}
+
 pkv_status pkv_append_paged_kv(const void* append_k, const void* append_v, int32_t nnz,
                                const int32_t* batch_indices_d, const int32_t* positions_d,
                                void* k_cache, void* v_cache, const pkv_paged_kv* layout,

@@ -34,7 +34,7 @@ PKV_ERR_HIP = 5
 # dtypes
 PKV_F16, PKV_BF16, PKV_F32 = 0, 1, 2
 # plan kinds
-PKV_KIND_DECODE, PKV_KIND_PREFILL, PKV_KIND_CASCADE = 1, 2, 3
+PKV_KIND_DECODE, PKV_KIND_PREFILL, PKV_KIND_CASCADE, PKV_KIND_BLOCK_SPARSE = 1, 2, 3, 4
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -115,6 +115,12 @@ _lib_merge_state_in_place = _sig("pkv_merge_state_in_place", _I32,
                                  [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P])
 _lib_merge_states = _sig("pkv_merge_states", _I32,
                          [_P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _P])
+_lib_block_sparse_plan = _sig("pkv_block_sparse_plan", _I32,
+                              [_I32P, _I32P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                               ctypes.POINTER(pkv_sched), _P, _SZ, _P, _SZ, _P, _SZ, _P,
+                               ctypes.POINTER(pkv_plan_info)])
+_lib_block_sparse_run = _sig("pkv_block_sparse_run", _I32,
+                             [ctypes.POINTER(pkv_plan_info), _P, _P, _P, _P, _P, _F32, _P, _P, _P])
 _lib_append_paged_kv = _sig("pkv_append_paged_kv", _I32,
                             [_P, _P, _I32, _P, _P, _P, _P, ctypes.POINTER(pkv_paged_kv), _P, _P,
                              _P, _I32, _P])
@@ -460,6 +466,35 @@ def pkv_cascade_run(plan: pkv_plan_info, q, k_cache, v_cache, prefix_indices_d, 
                             _ptr(prefix_indices_d), suffix_indptr_d.data_ptr(),
                             suffix_indices_d.data_ptr(), float(sm_scale), o.data_ptr(), _ptr(lse),
                             _stream(stream)), "pkv_cascade_run")
+    return o, lse
+
+
+def pkv_block_sparse_plan(bsr_indptr, bsr_indices, num_qo_tokens, num_kv_tokens, row_block,
+                          col_block, num_qo_heads, num_kv_heads, head_dim, dtype,
+                          workspace: Workspace, sched=None, stream=None) -> pkv_plan_info:
+    """Plan block-sparse attention over query blocks of row_block tokens and key blocks of
+    col_block tokens; (bsr_indptr, bsr_indices) are host arrays (BSR over the blocks)."""
+    ip = _host_i32(bsr_indptr)
+    ix = _host_i32(bsr_indices) if len(bsr_indices) else np.zeros(1, np.int32)
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+
+    def call(ws, info):
+        return _lib_block_sparse_plan(_i32p(ip), _i32p(ix), len(ip) - 1, int(num_qo_tokens),
+                                      int(num_kv_tokens), int(row_block), int(col_block),
+                                      num_qo_heads, num_kv_heads, head_dim, code, _sched_arg(sched),
+                                      *ws.args(), _stream(stream), ctypes.byref(info))
+    return _plan_with_growth(call, workspace, "pkv_block_sparse_plan")
+
+
+def pkv_block_sparse_run(plan: pkv_plan_info, q, k, v, bsr_indptr_d, bsr_indices_d,
+                         sm_scale: float, o=None, lse=None, stream=None):
+    """q [N_q, Hq, D], k / v [N_kv, Hkv, D] -> (o like q, lse [N_q, Hq] float32)."""
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(_lib_block_sparse_run(ctypes.byref(plan), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                 bsr_indptr_d.data_ptr(), bsr_indices_d.data_ptr(), float(sm_scale),
+                                 o.data_ptr(), _ptr(lse), _stream(stream)), "pkv_block_sparse_run")
     return o, lse
 
 

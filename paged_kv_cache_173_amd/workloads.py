@@ -318,3 +318,49 @@ SMALL = {
                             **kw),
     4: lambda **kw: long_decode(seed=173104, batch=2, kv_len=9000, **kw),
 }
+
+
+@dataclass
+class BlockSparseWorkload:
+    """Queries, dense keys / values and a BSR block mask over them."""
+    kind = "block_sparse"        # (class attribute, not a field)
+    dtype: str
+    num_qo_heads: int
+    num_kv_heads: int
+    head_dim: int
+    sm_scale: float
+    q: np.ndarray                # [N_q, Hq, D] bit patterns
+    k: np.ndarray                # [N_kv, Hkv, D]
+    v: np.ndarray
+    bsr_indptr: np.ndarray       # int32 [num_block_rows + 1]
+    bsr_indices: np.ndarray      # int32, ascending within each block row
+    row_block: int
+    col_block: int
+    meta: dict = field(default_factory=dict)
+
+
+def block_sparse(seed=173006, num_qo_tokens=8192, num_kv_tokens=8192, row_block=64, col_block=64,
+                 density=0.25, num_qo_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16",
+                 diagonal=True, empty_rows=()):
+    """A random block mask: each (block row, key block) pair is kept with probability
+    ``density`` (and the diagonal block always when ``diagonal``); block rows listed in
+    ``empty_rows`` keep nothing. Draw order: the mask (one uniform per block pair, row
+    major), q, k, v."""
+    rng = np.random.default_rng(seed)
+    mb = (num_qo_tokens + row_block - 1) // row_block
+    nb = (num_kv_tokens + col_block - 1) // col_block
+    keep = rng.random((mb, nb)) < density
+    if diagonal:
+        for i in range(min(mb, nb)):
+            keep[i, i] = True
+    for i in empty_rows:
+        keep[i, :] = False
+    indptr = np.zeros(mb + 1, dtype=np.int32)
+    indptr[1:] = np.cumsum(keep.sum(axis=1))
+    indices = np.nonzero(keep)[1].astype(np.int32)        # row-major: ascending within a row
+    q = normal_bits(rng, (num_qo_tokens, num_qo_heads, head_dim), dtype)
+    k = normal_bits(rng, (num_kv_tokens, num_kv_heads, head_dim), dtype)
+    v = normal_bits(rng, (num_kv_tokens, num_kv_heads, head_dim), dtype)
+    return BlockSparseWorkload(dtype, num_qo_heads, num_kv_heads, head_dim,
+                               1.0 / math.sqrt(head_dim), q, k, v, indptr, indices, row_block,
+                               col_block, meta={"seed": seed, "density": density})
