@@ -24,6 +24,9 @@ docs.flashinfer.ai index "Welcome to FlashInfer's documentation!"):
   "Append new K/V tensors to Paged KV-Cache", with the page walk above.
 * block-sparse attention: docs index "flashinfer.sparse" >
   "BlockSparseAttentionWrapper", with exact attention over a block mask.
+* attention variants (sliding window, logit soft cap, attention sinks), named
+  in the article "FlashInfer", section "Custom attention templates"; their
+  formulas are this oracle's readings, stated in ``variants.py``.
 
 Every function is pinned by tests under ``tests/`` (brute force on tiny inputs,
 closed forms, invariants, hand-worked golden fixtures). No function here is
@@ -47,3 +50,10 @@ from .attention import (  # noqa: F401
 from .plan import plan_spec, PlanSpec  # noqa: F401
 from .append import append_positions, append_paged_kv  # noqa: F401
 from .block_sparse import block_mask, block_sparse_attention  # noqa: F401
+from .variants import (  # noqa: F401
+    capped_logits,
+    window_visible,
+    variant_state,
+    batch_decode_variant,
+    batch_prefill_variant,
+)

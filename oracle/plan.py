@@ -18,16 +18,22 @@ Rule (all integer arithmetic; ceil(a / b) for b > 0):
     128 rows). Request b has tiles_b = ceil(Q_b * G / rows_per_tile).
 2.  KV extent of a tile. kv_end = L_b, or with the bottom-right causal mask
     kv_end = clamp(L_b - Q_b + t_last + 1, 0, L_b), where t_last is the query
-    token of the tile's last row. pages = ceil(kv_end / P).
+    token of the tile's last row. With a sliding window of W >= 0 keys to the
+    left (``window_left``; W < 0: none) the extent starts at
+    kv_lo = max(0, L_b - Q_b + t_first - W) (t_first: the query token of the
+    tile's first row), else kv_lo = 0. The tile's pages run from
+    p_lo = floor(kv_lo / P) to p_hi = ceil(kv_end / P);
+    pages = max(0, p_hi - p_lo).
 3.  work = Hkv * sum over (b, tile) of pages.  target = num_cus * wg_per_cu.
     c_min = max(1, ceil(min_chunk_tokens / P)).
     c = max(c_min, ceil(work / target))   (c = c_min when work = 0).
 4.  Each (b, tile, g) group splits into n_chunks = max(1, ceil(pages / c))
-    chunks; chunk j covers pages [j*c, min((j+1)*c, pages)) and KV tokens
-    [j*c*P, min((j+1)*c*P, kv_end)). A group with one chunk writes its final
-    output; a group with more chunks writes partial states into consecutive
-    partial slots, assigned to split groups in (b, tile, g) order, chunk j at
-    slot_begin + j; those groups are listed, in the same order, as merge groups.
+    chunks; chunk j covers pages [p_lo + j*c, min(p_lo + (j+1)*c, p_hi)) and
+    KV tokens [min((p_lo + j*c)*P, kv_end), min((p_lo + (j+1)*c)*P, kv_end)).
+    A group with one chunk writes its final output; a group with more chunks
+    writes partial states into consecutive partial slots, assigned to split
+    groups in (b, tile, g) order, chunk j at slot_begin + j; those groups are
+    listed, in the same order, as merge groups.
 5.  Items are executed longest first: sorted by descending KV token count,
     ties broken by ascending (b, tile, g, j).
 """
@@ -54,20 +60,23 @@ class PlanSpec:
 
 def plan_spec(qo_lens, kv_lens, page_size: int, num_kv_heads: int, group_size: int,
               rows_per_tile: int, causal: bool, num_cus: int, wg_per_cu: int,
-              min_chunk_tokens: int) -> PlanSpec:
+              min_chunk_tokens: int, window_left: int = -1) -> PlanSpec:
     """Apply the rule in the module docstring. ``qo_lens`` / ``kv_lens`` per request."""
     P, G = int(page_size), int(group_size)
     B = len(kv_lens)
-    tiles = []   # (b, tile, kv_end, pages)
+    tiles = []   # (b, tile, kv_end, p_lo, pages)
     for b in range(B):
         Q, L = int(qo_lens[b]), int(kv_lens[b])
         n_rows = Q * G
         for tile in range(_ceil_div(n_rows, rows_per_tile)):
+            first_row = tile * rows_per_tile
             last_row = min((tile + 1) * rows_per_tile, n_rows) - 1
-            t_last = last_row // G
+            t_first, t_last = first_row // G, last_row // G
             kv_end = min(max(L - Q + t_last + 1, 0), L) if causal else L
-            tiles.append((b, tile, kv_end, _ceil_div(kv_end, P)))
-    work = num_kv_heads * sum(t[3] for t in tiles)
+            kv_lo = max(0, L - Q + t_first - window_left) if window_left >= 0 else 0
+            p_lo = kv_lo // P
+            tiles.append((b, tile, kv_end, p_lo, max(0, _ceil_div(kv_end, P) - p_lo)))
+    work = num_kv_heads * sum(t[4] for t in tiles)
     target = num_cus * wg_per_cu
     c_min = max(1, _ceil_div(min_chunk_tokens, P))
     c = max(c_min, _ceil_div(work, target))
@@ -75,7 +84,7 @@ def plan_spec(qo_lens, kv_lens, page_size: int, num_kv_heads: int, group_size: i
     spec = PlanSpec(chunk_pages=c, rows_per_tile=rows_per_tile)
     raw = []      # (kv_count, b, tile, g, j, item)
     slot = 0
-    for (b, tile, kv_end, pages) in tiles:           # (b, tile) order
+    for (b, tile, kv_end, p_lo, pages) in tiles:     # (b, tile) order
         n_chunks = max(1, _ceil_div(pages, c))
         for g in range(num_kv_heads):                # then g
             slot_begin = slot if n_chunks > 1 else -1
@@ -83,8 +92,8 @@ def plan_spec(qo_lens, kv_lens, page_size: int, num_kv_heads: int, group_size: i
                 spec.merge_groups.append((b, tile, g, slot_begin, n_chunks))
                 slot += n_chunks
             for j in range(n_chunks):
-                p0, p1 = j * c, min((j + 1) * c, pages)
-                k0, k1 = min(j * c * P, kv_end), min((j + 1) * c * P, kv_end)
+                p0, p1 = p_lo + j * c, p_lo + min((j + 1) * c, pages)
+                k0, k1 = min(p0 * P, kv_end), min((p_lo + (j + 1) * c) * P, kv_end)
                 item = (b, g, tile, p0, p1, k0, k1, slot_begin + j if n_chunks > 1 else -1)
                 raw.append((k1 - k0, b, tile, g, j, item))
     raw.sort(key=lambda r: (-r[0], r[1], r[2], r[3], r[4]))

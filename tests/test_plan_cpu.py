@@ -153,3 +153,65 @@ def test_worked_chunk_sizes():
     # cascade level 0: 1 request, 128 query tokens x 4 heads = 4 tiles, 512 pages: c = 32
     sp = plan_spec([128], [8192], 16, 8, 4, 128, False, *s)
     assert sp.chunk_pages == 32 and len(sp.items) == 4 * 8 * 16
+
+
+def _window_case(rng):
+    B = int(rng.integers(1, 7))
+    P = int(rng.choice([1, 3, 16, 64]))
+    G = int(rng.choice([1, 4, 8]))
+    qo = rng.integers(1, 300, size=B)
+    kv = qo + rng.integers(0, 900, size=B)
+    kv[rng.random(B) < 0.2] = rng.integers(0, 50)          # some requests shorter than Q
+    W = int(rng.choice([0, 1, 15, 16, 100, 511, 5000]))
+    return B, P, G, qo, kv, W
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_window_extent_brute_force(seed):
+    """With a sliding window, each (b, tile, g) group's chunks cover exactly the pages
+    from the first to the last page holding a key that some row of the tile sees
+    (enumerated from the variant oracle's mask), in consecutive chunks of c pages."""
+    from oracle.variants import window_visible
+    rng = np.random.default_rng(1000 + seed)
+    B, P, G, qo, kv, W = _window_case(rng)
+    causal = seed % 3 != 0
+    decode = seed % 4 == 1
+    if decode:
+        qo = np.ones(B, dtype=np.int64)
+        causal = True
+    R = G if decode else 128
+    sched = SCHEDS[seed % len(SCHEDS)]
+    spec = plan_spec(qo, kv, P, 2, G, R, causal, *sched, window_left=W)
+    c = spec.chunk_pages
+    groups = {}
+    for it in spec.items:
+        groups.setdefault((it[0], it[2], it[1]), []).append(it)
+    for b in range(B):
+        Q, L = int(qo[b]), int(kv[b])
+        vis = window_visible(Q, L, W, causal)
+        for tile in range(-(-Q * G // R)):
+            rows = range(tile * R, min((tile + 1) * R, Q * G))
+            seen = np.zeros(L, dtype=bool)
+            for r in rows:
+                seen |= vis[r // G]
+            pages_seen = sorted({t // P for t in np.flatnonzero(seen)})
+            for g in range(2):
+                its = sorted(groups[(b, tile, g)], key=lambda x: x[3])
+                if not pages_seen:
+                    assert len(its) == 1 and its[0][5] == its[0][6]
+                    continue
+                lo, hi = pages_seen[0], pages_seen[-1] + 1
+                assert its[0][3] == lo and its[-1][4] == hi
+                assert its[0][5] == lo * P and its[-1][6] == max(np.flatnonzero(seen)) + 1
+                for a, nxt in zip(its, its[1:]):
+                    assert a[4] == nxt[3] and a[6] == nxt[5] and a[4] - a[3] == c
+                assert len(its) == -(-(hi - lo) // c)
+
+
+def test_window_off_is_the_plain_rule():
+    rng = np.random.default_rng(77)
+    for _ in range(6):
+        B, P, G, qo, kv, _ = _window_case(rng)
+        a = plan_spec(qo, kv, P, 2, G, 128, True, 256, 4, 256)
+        b = plan_spec(qo, kv, P, 2, G, 128, True, 256, 4, 256, window_left=-1)
+        assert a.items == b.items and a.merge_groups == b.merge_groups
