@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 
 typedef int32_t pkv_status;
 enum {
@@ -93,6 +93,34 @@ typedef struct pkv_paged_kv {
   pkv_dtype dtype; /* PKV_F16 or PKV_BF16 */
 } pkv_paged_kv;
 
+/* Attention variants of batch decode and prefill. The FlashInfer article
+ * (section "Custom attention templates") lists sliding windows, attention
+ * sinks and logit soft caps among the choices a model makes around the
+ * query-key product; the pages give no formulas, so these are this library's
+ * definitions:
+ *   window_left   W >= 0: a query at position p of its request's KV
+ *                 (prefill: p = i + L_b - Q_b; decode: p = L_b - 1) sees only
+ *                 keys t >= p - W (with the causal mask also t <= p, so at
+ *                 most W + 1 keys). -1: no window. Other values are invalid.
+ *                 The plan depends on it (items start at the page holding the
+ *                 first row's window start); plan and run must agree.
+ *   logits_soft_cap  c > 0: every scaled logit x = sm_scale * q.k becomes
+ *                 c * tanh(x / c) before the mask and the softmax. 0: off.
+ *                 Must be finite and >= 0.
+ *   sinks         device float32 [num_qo_heads] (4-byte aligned) or NULL:
+ *                 sinks[h] is the logit (natural log, the units of the capped
+ *                 scaled logits) of a virtual key with a zero value that joins
+ *                 the softmax of every row of query head h, once:
+ *                 O = sum_t e^{x_t} v_t / (e^{sinks[h]} + sum_t e^{x_t}) and
+ *                 LSE = ln(e^{sinks[h]} + sum_t e^{x_t}). A row that sees no
+ *                 key then gets O = 0 and LSE = sinks[h]; -inf is no sink.
+ * A NULL pkv_variant* means all three off. */
+typedef struct pkv_variant {
+  int32_t window_left;
+  float logits_soft_cap;
+  const float* sinks;
+} pkv_variant;
+
 /* Inputs of the work-chunk rule (see pkv_decode_plan). NULL means
  * pkv_default_sched() of the current device. */
 typedef struct pkv_sched {
@@ -110,6 +138,8 @@ typedef struct pkv_plan_part {
   int32_t rows_per_tile;    /* query rows per item (G for decode, 128 prefill) */
   int32_t num_slots;        /* partial states written by split groups         */
   int32_t causal;
+  int32_t window_left;      /* the sliding window the plan was made for (-1: none) */
+  int32_t reserved;
   int64_t items_off;        /* int ws: int32 [num_items][8]                   */
   int64_t groups_off;       /* int ws: int32 [num_groups][8]                  */
   int64_t kv_len_off;       /* int ws: int32 [batch] KV length per request    */
@@ -167,28 +197,32 @@ pkv_status pkv_default_sched_for(pkv_kind kind, int32_t device, pkv_sched* out);
  * Rule (integer arithmetic, ceil(a/b) rounding up):
  *   rows of request b are GQA-packed (row r = query token r/G, head
  *   g*G + r%G); a tile holds rows_per_tile rows (decode: G; prefill: 128);
- *   a tile's KV extent is L_b, or with the causal mask
+ *   a tile's KV extent ends at kv_end = L_b, or with the causal mask
  *   clamp(L_b - Q_b + t_last + 1, 0, L_b) (t_last = query token of its last
- *   row); pages(tile) = ceil(extent / P);
+ *   row), and starts at kv_lo = 0, or with a sliding window W >= 0
+ *   max(0, L_b - Q_b + t_first - W) (t_first = query token of its first row);
+ *   p_lo = floor(kv_lo / P), pages(tile) = max(0, ceil(kv_end / P) - p_lo);
  *   work = Hkv * sum pages(tile); target = num_cus * wg_per_cu;
  *   c = max(max(1, ceil(min_chunk_tokens / P)), ceil(work / target));
  *   each (b, tile, g) group splits into max(1, ceil(pages / c)) chunks, chunk
- *   j covering pages [j*c, min((j+1)*c, pages)) and tokens
- *   [j*c*P, min((j+1)*c*P, extent)); split groups get consecutive partial
- *   slots in (b, tile, g) order; items run longest first (descending token
- *   count, ties by ascending b, tile, g, j).
+ *   j covering pages [p_lo + j*c, p_lo + min((j+1)*c, pages)) and tokens
+ *   [min((p_lo + j*c)*P, kv_end), min((p_lo + (j+1)*c)*P, kv_end)); split
+ *   groups get consecutive partial slots in (b, tile, g) order; items run
+ *   longest first (descending token count, ties by ascending b, tile, g, j).
  * Outputs: items_out[num_items][8] = {b, g, tile, page_begin, page_end,
  *   kv_begin, kv_end, slot (-1 = writes the final output)};
  *   groups_out[num_groups][8] = {b, tile, g, slot_begin, num_chunks, 0, 0, 0};
  *   counts_out[4] = {num_items, num_groups, chunk_pages, num_slots}.
  * qo_indptr_h may be NULL for decode (kind PKV_KIND_DECODE, one query token
- * per request). Returns WORKSPACE_TOO_SMALL (counts still filled) when
- * items_cap / groups_cap are too small.
+ * per request). window_left as in pkv_variant (-1: none). Returns
+ * WORKSPACE_TOO_SMALL (counts still filled) when items_cap / groups_cap are
+ * too small.
  * ------------------------------------------------------------------------- */
 pkv_status pkv_plan_host(pkv_kind kind, const int32_t* qo_indptr_h, const int32_t* kv_indptr_h,
                          const int32_t* last_page_len_h, int32_t batch, int32_t num_qo_heads,
                          int32_t num_kv_heads, int32_t page_size, int32_t causal,
-                         const pkv_sched* sched, int32_t* items_out, int32_t items_cap,
+                         int32_t window_left, const pkv_sched* sched, int32_t* items_out,
+                         int32_t items_cap,
                          int32_t* groups_out, int32_t groups_cap, int32_t* counts_out);
 
 /* ---------------------------------------------------------------------------
@@ -203,18 +237,23 @@ pkv_status pkv_plan_host(pkv_kind kind, const int32_t* qo_indptr_h, const int32_
  * if any group split, the merge kernel. q [batch, Hq, 128], o like q
  * (same dtype as the cache), lse [batch, Hq] float32 or NULL.
  * sm_scale multiplies q.k (usually 1/sqrt(head_dim)).
+ * variant (plan: only its window_left is used; run: all of it; NULL = none)
+ * selects the attention variants of pkv_variant; the run returns
+ * PKV_ERR_PLAN_MISMATCH when its window_left differs from the plan's.
  * Needs 1 <= G <= 16.
  * ------------------------------------------------------------------------- */
 pkv_status pkv_decode_plan(const int32_t* kv_indptr_h, const int32_t* last_page_len_h,
                            int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
                            int32_t head_dim, int32_t page_size, pkv_dtype dtype,
-                           const pkv_sched* sched, void* int_ws, size_t int_ws_bytes,
-                           void* float_ws, size_t float_ws_bytes, void* host_ws,
-                           size_t host_ws_bytes, void* stream, pkv_plan_info* out);
+                           const pkv_variant* variant, const pkv_sched* sched, void* int_ws,
+                           size_t int_ws_bytes, void* float_ws, size_t float_ws_bytes,
+                           void* host_ws, size_t host_ws_bytes, void* stream,
+                           pkv_plan_info* out);
 
 pkv_status pkv_decode_run(const pkv_plan_info* plan, const void* q, const pkv_paged_kv* kv,
                           const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
-                          float sm_scale, void* o, float* lse, void* stream);
+                          float sm_scale, const pkv_variant* variant, void* o, float* lse,
+                          void* stream);
 
 /* As pkv_decode_run, and records `attention_done` (a hipEvent_t passed as
  * void*, created by the caller; NULL = none) on `stream` right after the
@@ -222,8 +261,8 @@ pkv_status pkv_decode_run(const pkv_plan_info* plan, const void* q, const pkv_pa
  * the two kernels separately. */
 pkv_status pkv_decode_run_timed(const pkv_plan_info* plan, const void* q, const pkv_paged_kv* kv,
                                 const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
-                                float sm_scale, void* o, float* lse, void* stream,
-                                void* attention_done);
+                                float sm_scale, const pkv_variant* variant, void* o, float* lse,
+                                void* stream, void* attention_done);
 
 /* ---------------------------------------------------------------------------
  * Batch paged prefill / append: Q_b = qo_indptr[b+1]-qo_indptr[b] query
@@ -231,27 +270,28 @@ pkv_status pkv_decode_run_timed(const pkv_plan_info* plan, const void* q, const 
  * bottom-right mask: query i sees key t iff t <= i + L_b - Q_b (rows with no
  * visible key give O = 0, LSE = -inf). causal=0 lets every query see all L_b
  * keys. q / o [total_qo, Hq, 128], lse [total_qo, Hq] float32 or NULL.
- * Plan and workspace rules as for decode. Needs G <= 128.
+ * Plan, workspace and variant rules as for decode. Needs G <= 128.
  * ------------------------------------------------------------------------- */
 pkv_status pkv_prefill_plan(const int32_t* qo_indptr_h, const int32_t* kv_indptr_h,
                             const int32_t* last_page_len_h, int32_t batch, int32_t num_qo_heads,
                             int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
-                            pkv_dtype dtype, int32_t causal, const pkv_sched* sched, void* int_ws,
-                            size_t int_ws_bytes, void* float_ws, size_t float_ws_bytes,
-                            void* host_ws, size_t host_ws_bytes, void* stream,
-                            pkv_plan_info* out);
+                            pkv_dtype dtype, int32_t causal, const pkv_variant* variant,
+                            const pkv_sched* sched, void* int_ws, size_t int_ws_bytes,
+                            void* float_ws, size_t float_ws_bytes, void* host_ws,
+                            size_t host_ws_bytes, void* stream, pkv_plan_info* out);
 
 pkv_status pkv_prefill_run(const pkv_plan_info* plan, const void* q, const pkv_paged_kv* kv,
                            const int32_t* qo_indptr_d, const int32_t* kv_indptr_d,
-                           const int32_t* kv_indices_d, float sm_scale, void* o, float* lse,
-                           void* stream);
+                           const int32_t* kv_indices_d, float sm_scale,
+                           const pkv_variant* variant, void* o, float* lse, void* stream);
 
 /* As pkv_prefill_run, recording `attention_done` after the attention kernel
  * (see pkv_decode_run_timed). */
 pkv_status pkv_prefill_run_timed(const pkv_plan_info* plan, const void* q, const pkv_paged_kv* kv,
                                  const int32_t* qo_indptr_d, const int32_t* kv_indptr_d,
-                                 const int32_t* kv_indices_d, float sm_scale, void* o, float* lse,
-                                 void* stream, void* attention_done);
+                                 const int32_t* kv_indices_d, float sm_scale,
+                                 const pkv_variant* variant, void* o, float* lse, void* stream,
+                                 void* attention_done);
 
 /* ---------------------------------------------------------------------------
  * Single-request decode over a contiguous NHD cache k, v [kv_len, Hkv, 128]

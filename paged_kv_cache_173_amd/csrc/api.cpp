@@ -151,6 +151,44 @@ pkv_status check_plan(const pkv_plan_info* plan, pkv_kind kind) {
   return PKV_OK;
 }
 
+// The window of a plan call's variant (-1 for none), validated.
+pkv_status plan_window(const pkv_variant* v, int32_t* window_left) {
+  *window_left = v != nullptr ? v->window_left : -1;
+  if (*window_left < -1) return fail(PKV_ERR_INVALID_ARG, "window_left must be -1 or >= 0");
+  return PKV_OK;
+}
+
+// Validates a run call's variant against the plan part and fills the
+// kernels' variant arguments (all off for NULL).
+pkv_status resolve_variant(const pkv_variant* v, const pkv_plan_part& part, float sm_scale,
+                           pkv::VariantArgs* out) {
+  *out = pkv::VariantArgs{-1, 0.f, 0.f, nullptr};
+  int32_t w;
+  pkv_status st;
+  if ((st = plan_window(v, &w))) return st;
+  if (w != part.window_left)
+    return fail(PKV_ERR_PLAN_MISMATCH, "window_left differs from the one the plan was made for");
+  if (v == nullptr) return PKV_OK;
+  const float c = v->logits_soft_cap;
+  if (!(c >= 0.f) || c > 3.0e38f)
+    return fail(PKV_ERR_INVALID_ARG, "logits_soft_cap must be finite and >= 0");
+  if (reinterpret_cast<uintptr_t>(v->sinks) % 4 != 0)
+    return fail(PKV_ERR_INVALID_ARG, "sinks must be 4-byte aligned");
+  out->window_left = w;
+  out->sinks = v->sinks;
+  if (c > 0.f) {
+    const double cin = 2.0 * 1.4426950408889634 * sm_scale / c;
+    const double cout = static_cast<double>(c) / sm_scale;
+    if (!(cin < 3.0e38) || !(cout < 3.0e38) || !(cin > 1e-37) || !(cout > 1e-37))
+      return fail(PKV_ERR_INVALID_ARG, "logits_soft_cap out of range for this sm_scale");
+    out->cap_in = static_cast<float>(cin);
+    out->cap_out = static_cast<float>(cout);
+  }
+  return PKV_OK;
+}
+
+const pkv::VariantArgs kNoVariant{-1, 0.f, 0.f, nullptr};
+
 struct Layout {
   int64_t int_bytes = 0;
   int64_t float_bytes = 0;
@@ -158,13 +196,14 @@ struct Layout {
 
 // Places one part's tables and partial states at the current end of each workspace.
 void place_part(const pkv::HostPlan& hp, int64_t batch, int32_t rows_per_tile, int32_t causal,
-                Layout* lay, pkv_plan_part* part) {
+                Layout* lay, pkv_plan_part* part, int32_t window_left = -1) {
   part->num_items = static_cast<int32_t>(hp.items.size());
   part->num_groups = static_cast<int32_t>(hp.groups.size());
   part->chunk_pages = hp.chunk_pages;
   part->rows_per_tile = rows_per_tile;
   part->num_slots = hp.num_slots;
   part->causal = causal;
+  part->window_left = window_left;
   part->items_off = lay->int_bytes;
   lay->int_bytes = align_up(lay->int_bytes + static_cast<int64_t>(hp.items.size()) * 32);
   part->groups_off = lay->int_bytes;
@@ -238,7 +277,7 @@ void fill_header(pkv_plan_info* out, pkv_kind kind, pkv_dtype dtype, int32_t bat
 
 pkv::PlanInput make_input(const std::vector<int64_t>& qo, const std::vector<int64_t>& kv,
                           int32_t page_size, int32_t hkv, int32_t G, int32_t rows, bool causal,
-                          const pkv_sched& s) {
+                          const pkv_sched& s, int32_t window_left = -1) {
   pkv::PlanInput in{};
   in.qo_lens = qo.data();
   in.kv_lens = kv.data();
@@ -248,6 +287,7 @@ pkv::PlanInput make_input(const std::vector<int64_t>& qo, const std::vector<int6
   in.group_size = G;
   in.rows_per_tile = rows;
   in.causal = causal;
+  in.window_left = window_left;
   in.num_cus = s.num_cus;
   in.wg_per_cu = s.wg_per_cu;
   in.min_chunk_tokens = s.min_chunk_tokens;
@@ -271,7 +311,8 @@ pkv_status run_decode_part(const pkv_plan_info* plan, const pkv_plan_part& part,
                            const pkv_paged_kv* kv, const int32_t* kv_indptr_d,
                            const int32_t* kv_indices_d, float sm_scale, void* o, float* lse,
                            pkv::OutKind out_kind, hipStream_t stream,
-                           hipEvent_t attention_done = nullptr) {
+                           hipEvent_t attention_done = nullptr,
+                           const pkv::VariantArgs& var = kNoVariant) {
   const int32_t G = plan->num_qo_heads / plan->num_kv_heads;
   pkv::DecodeArgs a{};
   a.q = q;
@@ -291,6 +332,8 @@ pkv_status run_decode_part(const pkv_plan_info* plan, const pkv_plan_part& part,
   a.lse = lse;
   a.part_o = f_at(plan->float_ws, part.part_o_off);
   a.part_lse = f_at(plan->float_ws, part.part_lse_off);
+  a.kv_lens = i_at(plan->int_ws, part.kv_len_off);
+  a.var = var;
   hipError_t e = pkv::launch_decode(a, plan->dtype, out_kind, page_mode(plan->page_size),
                                     part.num_items, stream);
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
@@ -307,6 +350,7 @@ pkv_status run_decode_part(const pkv_plan_info* plan, const pkv_plan_part& part,
     m.part_lse = a.part_lse;
     m.o = o;
     m.lse = lse;
+    m.sinks = var.sinks;
     e = pkv::launch_merge_groups(m, plan->dtype, out_kind, part.num_groups, stream);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
   }
@@ -318,7 +362,8 @@ pkv_status run_prefill_part(const pkv_plan_info* plan, const pkv_plan_part& part
                             const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
                             float sm_scale, void* o, float* lse, int32_t num_qo_heads,
                             pkv::OutKind out_kind, hipStream_t stream,
-                            hipEvent_t attention_done = nullptr) {
+                            hipEvent_t attention_done = nullptr,
+                            const pkv::VariantArgs& var = kNoVariant) {
   const int32_t G = num_qo_heads / plan->num_kv_heads;
   pkv::PrefillArgs a{};
   a.q = q;
@@ -341,6 +386,7 @@ pkv_status run_prefill_part(const pkv_plan_info* plan, const pkv_plan_part& part
   a.lse = lse;
   a.part_o = f_at(plan->float_ws, part.part_o_off);
   a.part_lse = f_at(plan->float_ws, part.part_lse_off);
+  a.var = var;
   hipError_t e = pkv::launch_prefill(a, plan->dtype, out_kind, page_mode(plan->page_size),
                                      part.num_items, stream);
   if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
@@ -358,6 +404,7 @@ pkv_status run_prefill_part(const pkv_plan_info* plan, const pkv_plan_part& part
     m.part_lse = a.part_lse;
     m.o = o;
     m.lse = lse;
+    m.sinks = var.sinks;
     e = pkv::launch_merge_groups(m, plan->dtype, out_kind, part.num_groups, stream);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
   }
@@ -403,8 +450,9 @@ pkv_status pkv_default_sched_for(pkv_kind kind, int32_t device, pkv_sched* out) 
 pkv_status pkv_plan_host(pkv_kind kind, const int32_t* qo_indptr_h, const int32_t* kv_indptr_h,
                          const int32_t* last_page_len_h, int32_t batch, int32_t num_qo_heads,
                          int32_t num_kv_heads, int32_t page_size, int32_t causal,
-                         const pkv_sched* sched, int32_t* items_out, int32_t items_cap,
-                         int32_t* groups_out, int32_t groups_cap, int32_t* counts_out) {
+                         int32_t window_left, const pkv_sched* sched, int32_t* items_out,
+                         int32_t items_cap, int32_t* groups_out, int32_t groups_cap,
+                         int32_t* counts_out) {
   if (sched == nullptr) return fail(PKV_ERR_INVALID_ARG, "pkv_plan_host needs an explicit sched");
   if (counts_out == nullptr) return fail(PKV_ERR_INVALID_ARG, "counts_out is NULL");
   pkv_status st = check_sched(sched);
@@ -412,6 +460,8 @@ pkv_status pkv_plan_host(pkv_kind kind, const int32_t* qo_indptr_h, const int32_
   if ((st = check_heads(num_qo_heads, num_kv_heads))) return st;
   if (kind != PKV_KIND_DECODE && kind != PKV_KIND_PREFILL)
     return fail(PKV_ERR_INVALID_ARG, "kind must be PKV_KIND_DECODE or PKV_KIND_PREFILL");
+  if (window_left < -1) return fail(PKV_ERR_INVALID_ARG, "window_left must be -1 or >= 0");
+  if (window_left < -1) return fail(PKV_ERR_INVALID_ARG, "window_left must be -1 or >= 0");
   std::vector<int64_t> kv_lens, qo_lens;
   if ((st = check_page_table(kv_indptr_h, last_page_len_h, batch, page_size, &kv_lens))) return st;
   const int32_t G = num_qo_heads / num_kv_heads;
@@ -427,7 +477,7 @@ pkv_status pkv_plan_host(pkv_kind kind, const int32_t* qo_indptr_h, const int32_
   pkv::HostPlan hp;
   std::string err;
   if (!pkv::build_plan(make_input(qo_lens, kv_lens, page_size, num_kv_heads, G, rows, causal != 0,
-                                  *sched),
+                                  *sched, window_left),
                        &hp, &err))
     return fail(PKV_ERR_INVALID_ARG, err);
   counts_out[0] = static_cast<int32_t>(hp.items.size());
@@ -451,11 +501,14 @@ pkv_status pkv_plan_host(pkv_kind kind, const int32_t* qo_indptr_h, const int32_
 pkv_status pkv_decode_plan(const int32_t* kv_indptr_h, const int32_t* last_page_len_h,
                            int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
                            int32_t head_dim, int32_t page_size, pkv_dtype dtype,
-                           const pkv_sched* sched, void* int_ws, size_t int_ws_bytes,
-                           void* float_ws, size_t float_ws_bytes, void* host_ws,
-                           size_t host_ws_bytes, void* stream, pkv_plan_info* out) {
+                           const pkv_variant* variant, const pkv_sched* sched, void* int_ws,
+                           size_t int_ws_bytes, void* float_ws, size_t float_ws_bytes,
+                           void* host_ws, size_t host_ws_bytes, void* stream,
+                           pkv_plan_info* out) {
   if (out == nullptr) return fail(PKV_ERR_INVALID_ARG, "out is NULL");
   pkv_status st;
+  int32_t window_left;
+  if ((st = plan_window(variant, &window_left))) return st;
   if ((st = check_heads(num_qo_heads, num_kv_heads))) return st;
   if ((st = check_head_dim_dtype(head_dim, dtype))) return st;
   const int32_t G = num_qo_heads / num_kv_heads;
@@ -468,13 +521,14 @@ pkv_status pkv_decode_plan(const int32_t* kv_indptr_h, const int32_t* last_page_
   std::vector<int64_t> qo_lens(batch, 1);
   pkv::HostPlan hp;
   std::string err;
-  if (!pkv::build_plan(make_input(qo_lens, kv_lens, page_size, num_kv_heads, G, G, false, s), &hp,
-                       &err))
+  if (!pkv::build_plan(
+          make_input(qo_lens, kv_lens, page_size, num_kv_heads, G, G, false, s, window_left), &hp,
+          &err))
     return fail(PKV_ERR_INVALID_ARG, err);
   fill_header(out, PKV_KIND_DECODE, dtype, batch, num_qo_heads, num_kv_heads, head_dim, page_size,
               batch, s);
   Layout lay;
-  place_part(hp, batch, G, 0, &lay, &out->part[0]);
+  place_part(hp, batch, G, 0, &lay, &out->part[0], window_left);
   if (host_ws != nullptr && host_ws_bytes >= static_cast<size_t>(lay.int_bytes))
     write_part(hp, kv_lens, out->part[0], static_cast<char*>(host_ws));
   if ((st = commit_plan(lay, int_ws, int_ws_bytes, float_ws, float_ws_bytes, host_ws,
@@ -485,26 +539,29 @@ pkv_status pkv_decode_plan(const int32_t* kv_indptr_h, const int32_t* last_page_
 
 pkv_status pkv_decode_run(const pkv_plan_info* plan, const void* q, const pkv_paged_kv* kv,
                           const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
-                          float sm_scale, void* o, float* lse, void* stream) {
-  return pkv_decode_run_timed(plan, q, kv, kv_indptr_d, kv_indices_d, sm_scale, o, lse, stream,
-                              nullptr);
+                          float sm_scale, const pkv_variant* variant, void* o, float* lse,
+                          void* stream) {
+  return pkv_decode_run_timed(plan, q, kv, kv_indptr_d, kv_indices_d, sm_scale, variant, o, lse,
+                              stream, nullptr);
 }
 
 pkv_status pkv_decode_run_timed(const pkv_plan_info* plan, const void* q, const pkv_paged_kv* kv,
                                 const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
-                                float sm_scale, void* o, float* lse, void* stream,
-                                void* attention_done) {
+                                float sm_scale, const pkv_variant* variant, void* o, float* lse,
+                                void* stream, void* attention_done) {
   pkv_status st;
   if ((st = check_scale(sm_scale))) return st;
   if ((st = check_plan(plan, PKV_KIND_DECODE))) return st;
   if ((st = check_kv(kv, plan))) return st;
+  pkv::VariantArgs var;
+  if ((st = resolve_variant(variant, plan->part[0], sm_scale, &var))) return st;
   if (plan->batch > 0 && (q == nullptr || o == nullptr || kv_indptr_d == nullptr ||
                           kv_indices_d == nullptr))
     return fail(PKV_ERR_INVALID_ARG, "q, o, kv_indptr or kv_indices is NULL");
   if (!aligned16(q) || !aligned16(o)) return fail(PKV_ERR_INVALID_ARG, "q / o must be 16-byte aligned");
   if ((st = run_decode_part(plan, plan->part[0], q, kv, kv_indptr_d, kv_indices_d, sm_scale, o,
                             lse, pkv::kOutStorage, static_cast<hipStream_t>(stream),
-                            static_cast<hipEvent_t>(attention_done))))
+                            static_cast<hipEvent_t>(attention_done), var)))
     return st;
   return ok();
 }
@@ -512,12 +569,14 @@ pkv_status pkv_decode_run_timed(const pkv_plan_info* plan, const void* q, const 
 pkv_status pkv_prefill_plan(const int32_t* qo_indptr_h, const int32_t* kv_indptr_h,
                             const int32_t* last_page_len_h, int32_t batch, int32_t num_qo_heads,
                             int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
-                            pkv_dtype dtype, int32_t causal, const pkv_sched* sched, void* int_ws,
-                            size_t int_ws_bytes, void* float_ws, size_t float_ws_bytes,
-                            void* host_ws, size_t host_ws_bytes, void* stream,
-                            pkv_plan_info* out) {
+                            pkv_dtype dtype, int32_t causal, const pkv_variant* variant,
+                            const pkv_sched* sched, void* int_ws, size_t int_ws_bytes,
+                            void* float_ws, size_t float_ws_bytes, void* host_ws,
+                            size_t host_ws_bytes, void* stream, pkv_plan_info* out) {
   if (out == nullptr) return fail(PKV_ERR_INVALID_ARG, "out is NULL");
   pkv_status st;
+  int32_t window_left;
+  if ((st = plan_window(variant, &window_left))) return st;
   if ((st = check_heads(num_qo_heads, num_kv_heads))) return st;
   if ((st = check_head_dim_dtype(head_dim, dtype))) return st;
   if (causal != 0 && causal != 1) return fail(PKV_ERR_INVALID_ARG, "causal must be 0 or 1");
@@ -536,13 +595,13 @@ pkv_status pkv_prefill_plan(const int32_t* qo_indptr_h, const int32_t* kv_indptr
   pkv::HostPlan hp;
   std::string err;
   if (!pkv::build_plan(make_input(qo_lens, kv_lens, page_size, num_kv_heads, G,
-                                  kRowsPerPrefillTile, causal != 0, s),
+                                  kRowsPerPrefillTile, causal != 0, s, window_left),
                        &hp, &err))
     return fail(PKV_ERR_INVALID_ARG, err);
   fill_header(out, PKV_KIND_PREFILL, dtype, batch, num_qo_heads, num_kv_heads, head_dim,
               page_size, static_cast<int32_t>(total_qo), s);
   Layout lay;
-  place_part(hp, batch, kRowsPerPrefillTile, causal, &lay, &out->part[0]);
+  place_part(hp, batch, kRowsPerPrefillTile, causal, &lay, &out->part[0], window_left);
   if (host_ws != nullptr && host_ws_bytes >= static_cast<size_t>(lay.int_bytes))
     write_part(hp, kv_lens, out->part[0], static_cast<char*>(host_ws));
   if ((st = commit_plan(lay, int_ws, int_ws_bytes, float_ws, float_ws_bytes, host_ws,
@@ -553,20 +612,23 @@ pkv_status pkv_prefill_plan(const int32_t* qo_indptr_h, const int32_t* kv_indptr
 
 pkv_status pkv_prefill_run(const pkv_plan_info* plan, const void* q, const pkv_paged_kv* kv,
                            const int32_t* qo_indptr_d, const int32_t* kv_indptr_d,
-                           const int32_t* kv_indices_d, float sm_scale, void* o, float* lse,
-                           void* stream) {
-  return pkv_prefill_run_timed(plan, q, kv, qo_indptr_d, kv_indptr_d, kv_indices_d, sm_scale, o,
-                               lse, stream, nullptr);
+                           const int32_t* kv_indices_d, float sm_scale,
+                           const pkv_variant* variant, void* o, float* lse, void* stream) {
+  return pkv_prefill_run_timed(plan, q, kv, qo_indptr_d, kv_indptr_d, kv_indices_d, sm_scale,
+                               variant, o, lse, stream, nullptr);
 }
 
 pkv_status pkv_prefill_run_timed(const pkv_plan_info* plan, const void* q, const pkv_paged_kv* kv,
                                  const int32_t* qo_indptr_d, const int32_t* kv_indptr_d,
-                                 const int32_t* kv_indices_d, float sm_scale, void* o, float* lse,
-                                 void* stream, void* attention_done) {
+                                 const int32_t* kv_indices_d, float sm_scale,
+                                 const pkv_variant* variant, void* o, float* lse, void* stream,
+                                 void* attention_done) {
   pkv_status st;
   if ((st = check_scale(sm_scale))) return st;
   if ((st = check_plan(plan, PKV_KIND_PREFILL))) return st;
   if ((st = check_kv(kv, plan))) return st;
+  pkv::VariantArgs var;
+  if ((st = resolve_variant(variant, plan->part[0], sm_scale, &var))) return st;
   if (plan->total_qo > 0 && (q == nullptr || o == nullptr || qo_indptr_d == nullptr ||
                              kv_indptr_d == nullptr || kv_indices_d == nullptr))
     return fail(PKV_ERR_INVALID_ARG, "q, o, qo_indptr, kv_indptr or kv_indices is NULL");
@@ -574,7 +636,7 @@ pkv_status pkv_prefill_run_timed(const pkv_plan_info* plan, const void* q, const
   if ((st = run_prefill_part(plan, plan->part[0], q, kv, qo_indptr_d, kv_indptr_d, kv_indices_d,
                              sm_scale, o, lse, plan->num_qo_heads, pkv::kOutStorage,
                              static_cast<hipStream_t>(stream),
-                             static_cast<hipEvent_t>(attention_done))))
+                             static_cast<hipEvent_t>(attention_done), var)))
     return st;
   return ok();
 }

@@ -36,6 +36,12 @@
 //   * -inf is a real IEEE -inf; exp2 of (-inf) - (-inf) is avoided by
 //     subtracting 0 when the running max is still -inf. An empty item yields
 //     O = 0, LSE = -inf.
+//   * Variants (VAR instances, paged modes; the FlashInfer article, section
+//     "Custom attention templates", names them): the scores of a block are
+//     soft-capped before the mask, tokens below the sliding window's start
+//     (L - 1 - window_left) are masked like tail tokens, and a head's sink
+//     joins the softmax in the epilogue of an item that writes the final row
+//     (split items leave it to the merge).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -48,8 +54,9 @@ constexpr int kBlock = 16;  // tokens per wave iteration
 // K/V pages are read once per call: stream them past the caches.
 constexpr int kCachePolicy = kCacheStream;
 
-template <class T, class OUT, int MODE>
+template <class T, class OUT, int MODE, bool VAR>
 __global__ __launch_bounds__(256, 3) void decode_kernel(const DecodeArgs a) {
+  static_assert(!VAR || MODE != kContiguous, "variants need the paged item table");
   using elem = typename T::elem;
   constexpr int D = kHeadDim;
   __shared__ float s_m[kWaves][16];
@@ -105,6 +112,12 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(const DecodeArgs a) {
   };
 
   const int last = t1 - 1;
+  // First token the query sees under the sliding window (VAR only).
+  int wlo = 0;
+  if constexpr (VAR) {
+    if (a.var.window_left >= 0) wlo = a.kv_lens[b] - 1 - a.var.window_left;
+  }
+  const bool capped = VAR && a.var.cap_out > 0.f;
 
   // Issue the K and V loads of 16-token block `blk`. Paged-uniform and
   // contiguous modes: one scalar buffer descriptor per block, based at the
@@ -168,8 +181,16 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(const DecodeArgs a) {
     const int tb = t0 + kBlock * blk;
     float x[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      x[i] = (tb + 4 * grp + i < t1) ? s[i] * a.scale_log2 : neg_inf();
+    for (int i = 0; i < 4; ++i) {
+      const int t = tb + 4 * grp + i;
+      float si = s[i];
+      bool vis = t < t1;
+      if constexpr (VAR) {
+        if (capped) si = soft_cap(si, a.var.cap_in, a.var.cap_out);
+        vis = vis && t >= wlo;
+      }
+      x[i] = vis ? si * a.scale_log2 : neg_inf();
+    }
     float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     bm = max_across_rows(bm);
     const float m_new = fmaxf(m_run, bm);
@@ -275,8 +296,15 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(const DecodeArgs a) {
     float M = s_m[0][row];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][row]);
+    // A sink (log2 domain) is one more term of the sum, with a zero value.
+    float sink = neg_inf();
+    if constexpr (VAR) {
+      if (a.var.sinks != nullptr && slot < 0) sink = a.var.sinks[g * G + row] * kLog2e;
+      M = fmaxf(M, sink);
+    }
     const float Mu = (M == neg_inf()) ? 0.f : M;
     float L = 0.f, O = 0.f;
+    if constexpr (VAR) L = fast_exp2(sink - Mu);
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float f = fast_exp2(s_m[w][row] - Mu);
@@ -297,15 +325,23 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(const DecodeArgs a) {
 
 template <class T, class OUT>
 hipError_t launch_decode_t(const DecodeArgs& a, PageMode mode, int32_t grid, hipStream_t s) {
+  if (variant_on(a.var)) {
+    if (mode == kContiguous) return hipErrorInvalidValue;
+    if (mode == kPagedUniform)
+      hipLaunchKernelGGL((decode_kernel<T, OUT, kPagedUniform, true>), dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<T, OUT, kPagedGeneric, true>), dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   switch (mode) {
     case kContiguous:
-      hipLaunchKernelGGL((decode_kernel<T, OUT, kContiguous>), dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((decode_kernel<T, OUT, kContiguous, false>), dim3(grid), dim3(256), 0, s, a);
       break;
     case kPagedUniform:
-      hipLaunchKernelGGL((decode_kernel<T, OUT, kPagedUniform>), dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((decode_kernel<T, OUT, kPagedUniform, false>), dim3(grid), dim3(256), 0, s, a);
       break;
     default:
-      hipLaunchKernelGGL((decode_kernel<T, OUT, kPagedGeneric>), dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((decode_kernel<T, OUT, kPagedGeneric, false>), dim3(grid), dim3(256), 0, s, a);
       break;
   }
   return hipGetLastError();
@@ -316,7 +352,7 @@ hipError_t launch_decode_t(const DecodeArgs& a, PageMode mode, int32_t grid, hip
 int32_t decode_occupancy() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&decode_kernel<F16, _Float16, kPagedUniform>), 256,
+          &n, reinterpret_cast<const void*>(&decode_kernel<F16, _Float16, kPagedUniform, false>), 256,
           0) != hipSuccess)
     return 0;
   return n;

@@ -30,6 +30,14 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // largest term is exp2(0) = 1).
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Logit soft cap of a raw score s: cap_out * tanh(y), y = s * cap_in / (2 log2 e),
+// with tanh(y) = 1 - 2 / (2^(2 y log2 e) + 1). Saturates to +-cap_out (2^x
+// gives inf or 0); the absolute error of the tanh is a few ulp of 1.
+__device__ __forceinline__ float soft_cap(float s, float cap_in, float cap_out) {
+  const float e = fast_exp2(s * cap_in);
+  return fmaf(-2.f * cap_out, __builtin_amdgcn_rcpf(e + 1.f), cap_out);
+}
+
 __device__ __forceinline__ u32x4 load_16B(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

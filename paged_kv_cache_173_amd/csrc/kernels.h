@@ -17,6 +17,27 @@ enum PageMode : int32_t {
 
 enum OutKind : int32_t { kOutStorage = 0, kOutF32 = 1 };
 
+// Attention variants shared by the decode and prefill kernels (all off:
+// window_left < 0, cap_out = 0, sinks = NULL; the launchers then pick the
+// plain kernels).
+//   * Sliding window: a row at position p sees keys t >= p - window_left.
+//   * Logit soft cap c: the raw score s = q.k becomes
+//     cap_out * tanh(s * sm_scale / c) with cap_out = c / sm_scale, so that
+//     sm_scale times it is c * tanh(sm_scale * s / c); the kernels form
+//     tanh(y) = 1 - 2 / (exp2(2 y log2 e) + 1) with cap_in = 2 log2(e) sm_scale / c.
+//   * Sinks: sinks[h] (natural log) joins the softmax of every row of query
+//     head h as a key with a zero value, once, where the final row is written.
+struct VariantArgs {
+  int32_t window_left = -1;
+  float cap_in = 0.f;
+  float cap_out = 0.f;
+  const float* sinks = nullptr;   // device [num_qo_heads] or NULL
+};
+
+inline bool variant_on(const VariantArgs& v) {
+  return v.window_left >= 0 || v.cap_out > 0.f || v.sinks != nullptr;
+}
+
 struct DecodeArgs {
   const void* q;            // [batch, Hq, 128] storage dtype
   const void* k;            // K page pool base
@@ -36,6 +57,8 @@ struct DecodeArgs {
   float* lse;                 // final LSE [batch*Hq] or NULL
   float* part_o;              // partial states [slot][G][128]
   float* part_lse;            // [slot][G]
+  const int32_t* kv_lens;     // device [batch] KV length per request (variants only)
+  VariantArgs var;
 };
 
 struct PrefillArgs {
@@ -57,6 +80,7 @@ struct PrefillArgs {
   float* lse;                 // [total_qo*Hq] or NULL
   float* part_o;              // [slot][128 rows][128]
   float* part_lse;            // [slot][128 rows]
+  VariantArgs var;
 };
 
 struct AppendArgs {
@@ -89,6 +113,7 @@ struct MergeGroupsArgs {
   const float* part_lse;
   void* o;
   float* lse;                 // or NULL
+  const float* sinks;         // device [num_qo_heads] sink logits, or NULL
 };
 
 // Workgroups of the decode / prefill kernel resident per CU (0 on error).

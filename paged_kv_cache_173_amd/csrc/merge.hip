@@ -76,10 +76,14 @@ __global__ __launch_bounds__(256) void merge_groups_kernel(const MergeGroupsArgs
   float M = neg_inf();
   for (int k = lane; k < n; k += 64) M = fmaxf(M, lse[static_cast<int64_t>(k) * R]);
   M = wave_max(M);
+  // An attention sink of the row's head is one more state (0, sink): it
+  // enters the maximum and the sum, and adds nothing to the output.
+  const float sink = a.sinks != nullptr ? a.sinks[orow % a.num_qo_heads] : neg_inf();
+  M = fmaxf(M, sink);
   const float Mu = (M == neg_inf()) ? 0.f : M;
   float L = 0.f;
   for (int k = lane; k < n; k += 64) L += fast_exp2((lse[static_cast<int64_t>(k) * R] - Mu) * kLog2e);
-  L = wave_sum(L);
+  L = wave_sum(L) + fast_exp2((sink - Mu) * kLog2e);
 
   float o0 = 0.f, o1 = 0.f;
   for (int k = wave; k < n; k += 4) {

@@ -12,7 +12,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct TileExtent {
   int32_t b, tile;
-  int64_t kv_end, pages;
+  int64_t kv_end, page_lo, pages;
 };
 
 struct Keyed {
@@ -28,7 +28,9 @@ bool build_plan(const PlanInput& in, HostPlan* out, std::string* err) {
   out->items.clear();
   out->groups.clear();
 
-  // Per (request, tile): the KV extent the tile's rows may see.
+  // Per (request, tile): the KV extent the tile's rows may see. It ends
+  // after the last row's causal limit and, with a sliding window, starts at
+  // the first row's window start (rounded down to a page).
   std::vector<TileExtent> tiles;
   int64_t page_sum = 0;
   for (int32_t b = 0; b < in.batch; ++b) {
@@ -42,8 +44,11 @@ bool build_plan(const PlanInput& in, HostPlan* out, std::string* err) {
         const int64_t q_last = last_row / G;
         extent = std::clamp<int64_t>(L - Q + q_last + 1, 0, L);
       }
-      const int64_t pages = ceil_div(extent, P);
-      tiles.push_back({b, static_cast<int32_t>(t), extent, pages});
+      int64_t kv_lo = 0;
+      if (in.window_left >= 0) kv_lo = std::max<int64_t>(0, L - Q + (t * R) / G - in.window_left);
+      const int64_t page_lo = kv_lo / P;
+      const int64_t pages = std::max<int64_t>(0, ceil_div(extent, P) - page_lo);
+      tiles.push_back({b, static_cast<int32_t>(t), extent, page_lo, pages});
       page_sum += pages;
     }
   }
@@ -81,10 +86,10 @@ bool build_plan(const PlanInput& in, HostPlan* out, std::string* err) {
         it.b = te.b;
         it.g = g;
         it.tile = te.tile;
-        it.page_begin = static_cast<int32_t>(j * c);
-        it.page_end = static_cast<int32_t>(std::min((j + 1) * c, te.pages));
-        const int64_t k0 = std::min(j * c * P, te.kv_end);
-        const int64_t k1 = std::min((j + 1) * c * P, te.kv_end);
+        it.page_begin = static_cast<int32_t>(te.page_lo + j * c);
+        it.page_end = static_cast<int32_t>(te.page_lo + std::min((j + 1) * c, te.pages));
+        const int64_t k0 = std::min((te.page_lo + j * c) * P, te.kv_end);
+        const int64_t k1 = std::min((te.page_lo + (j + 1) * c) * P, te.kv_end);
         it.kv_begin = static_cast<int32_t>(k0);
         it.kv_end = static_cast<int32_t>(k1);
         it.slot = n_chunks > 1 ? static_cast<int32_t>(slot_begin + j) : -1;

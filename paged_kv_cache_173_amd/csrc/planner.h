@@ -37,6 +37,7 @@ struct PlanInput {
   int32_t group_size;      // G = num_qo_heads / num_kv_heads
   int32_t rows_per_tile;   // G for decode, 128 for prefill
   bool causal;
+  int32_t window_left;     // W >= 0: a row at position p sees keys >= p - W; < 0: no window
   int32_t num_cus;
   int32_t wg_per_cu;
   int32_t min_chunk_tokens;

@@ -38,6 +38,13 @@
 //     accumulator of row l % 32 stays in lane l, so the rescale is lane-local.
 //   * The scale multiplies the fp32 scores (q is not pre-scaled), in the
 //     log2 domain; LSE = (m + log2 l) * ln 2.
+//   * Variants (VAR instances; the FlashInfer article, section "Custom
+//     attention templates", names them): a tile's scores are soft-capped as
+//     soon as they leave the MFMAs, before the mask; the sliding window masks
+//     keys below a row's window start in the same wave-uniform mask step as
+//     the causal limit (the plan already starts each item at the page of its
+//     first row's window); a head's sink joins the final sum of an item that
+//     writes the final row (split items leave it to the merge).
 #include <type_traits>
 
 #include "device_common.h"
@@ -118,7 +125,7 @@ __device__ __forceinline__ void store4(OUT* p, float x0, float x1, float x2, flo
 // state is rescaled a few times per row instead of on most tiles.
 constexpr float kRescaleSlack = 8.f;
 
-template <class T, class OUT, int MODE>
+template <class T, class OUT, int MODE, bool VAR>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   using elem = typename T::elem;
   constexpr int D = kHeadDim;
@@ -172,6 +179,19 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   // Keys past this one need a mask for some row of the wave (the causal
   // limit of the wave's first row, or the item's end).
   const int mask_from = a.causal ? min(k1 - 1, lim_wave) : k1 - 1;
+  // Sliding window (VAR): the row's first visible key, and the largest of
+  // them in the wave (its last row's): tiles starting below it need the
+  // window mask for some row of the wave.
+  int wlo = 0, win_from = 0;
+  if constexpr (VAR) {
+    if (a.var.window_left >= 0) {
+      wlo = lim - a.var.window_left;
+      win_from = (tile * kTileRows + 32 * wave + 31) / G + L - Q - a.var.window_left;
+    } else {
+      wlo = win_from = INT32_MIN / 4;
+    }
+  }
+  const bool capped = VAR && a.var.cap_out > 0.f;
 
   // q^T as the B operand: lane holds q[row lr][d = 16kk + 8*half .. +7].
   u32x4 qv[8];
@@ -269,9 +289,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
 
   // Row state. The exponent reference m_ref (log2 domain, scaled) is the row
   // maximum seen so far up to the lazy slack; weights are
-  // exp2(scale_log2 * s - m_ref) rounded once to the storage dtype, and both
-  // the normalisation of O and the LSE use the sum of those rounded weights
-  // (O is then an exact convex combination of V rows).
+  // exp2(scale_log2 * s - m_ref) rounded once to the storage dtype, and the
+  // normalisation of O uses the sum of those rounded weights (O is then an
+  // exact convex combination of V rows). The LSE needs the sum of the
+  // unrounded weights when the rounding is coarse: one bf16 rounding is off by
+  // up to 2^-8 relative, ln(1 + 2^-8) = 3.9e-3 in the LSE for a row with few
+  // keys, so bf16 keeps a second, fp32 sum; fp16's 2^-11 (4.9e-4) uses the
+  // rounded sum for both.
   float m_ref = neg_inf();
   float neg_m = 0.f;          // -m_ref, or 0 while m_ref = -inf
   // Raw-score threshold (m_ref + slack) / scale_log2: a tile needs the
@@ -279,7 +303,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   // it only moves the point at which the reference is refreshed).
   float thr = neg_inf();
   const float inv_scale_log2 = 1.f / a.scale_log2;
-  float l_run = 0.f;          // this lane's share of the row's weight sum
+  float l_run = 0.f;          // this lane's share of the row's rounded-weight sum
+  constexpr bool kExactLse = std::is_same_v<T, BF16>;
+  float l_lse = 0.f;          // ... and of its unrounded-weight sum (kExactLse)
   f32x16 acc[4];              // acc[mb][i]: row lr, d = 32mb + 8(i/4) + 4*half + i%4
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
@@ -324,7 +350,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   // causal limit (wave-uniform test; one compare and select per score).
   auto mask = [&](int ti, f32x16& s) {
     const int tb = k0 + ti * KT;
-    if (tb + KT - 1 > mask_from) {
+    if constexpr (VAR) {
+      if (capped) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = soft_cap(s[i], a.var.cap_in, a.var.cap_out);
+      }
+      if (tb + KT - 1 > mask_from || tb < win_from) {
+        const int tlast = (a.causal ? min(k1 - 1, lim) : k1 - 1) - (tb + 4 * half);
+        const int tfirst = wlo - (tb + 4 * half);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int off = 8 * (i >> 2) + (i & 3);
+          if (off > tlast || off < tfirst) s[i] = neg_inf();
+        }
+      }
+    } else if (tb + KT - 1 > mask_from) {
       const int tlast = (a.causal ? min(k1 - 1, lim) : k1 - 1) - (tb + 4 * half);
 #pragma unroll
       for (int i = 0; i < 16; ++i)
@@ -349,6 +389,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       neg_m = (m_new == neg_inf()) ? 0.f : -m_new;
       thr = (m_new == neg_inf()) ? neg_inf() : (m_new + kRescaleSlack) * inv_scale_log2;
       l_run *= alpha;
+      if constexpr (kExactLse) l_lse *= alpha;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) acc[mb] *= alpha;
     }
@@ -356,7 +397,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   // Weights of a tile, rounded to the storage dtype: pk[st] is the B operand
   // of 16-token step st of the PV product.
   auto weights = [&](const f32x16& s, u32x4 (&pk)[2]) {
-    float sum = l_run;
+    float sum = l_run, xsum = l_lse;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
@@ -365,9 +406,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
         const float x1 = fast_exp2(fmaf(s[8 * st + 2 * j + 1], a.scale_log2, neg_m));
         pk[st][j] = T::pack2(x0, x1);
         sum = T::add_pair(pk[st][j], sum);
+        if constexpr (kExactLse) xsum += x0 + x1;
       }
     }
     l_run = sum;
+    l_lse = xsum;
   };
   // O^T += V^T P^T over two 16-token steps. Step st covers tokens
   // 16st + 4*half + {0..3} (first read) and + {8..11} (second read), the
@@ -404,7 +447,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   // steps read the first two V operands of the PV product into vf[0..1].
   auto qk_weights = [&](const char* kt, u32x4 (&kf)[3], f32x16& s, const f32x16& sc,
                         u32x4 (&pk)[2], const char* vt, u32x4 (&vf)[3]) {
-    float sum = l_run;
+    float sum = l_run, xsum = l_lse;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       if (kk + 2 < 8) kf[(kk + 2) % 3] = k_read(kt, kk + 2);
@@ -414,9 +457,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       const float x1 = fast_exp2(fmaf(sc[2 * kk + 1], a.scale_log2, neg_m));
       pk[kk >> 2][kk & 3] = T::pack2(x0, x1);
       sum = T::add_pair(pk[kk >> 2][kk & 3], sum);
+      if constexpr (kExactLse) xsum += x0 + x1;
+      // Keep the running sums in this step (otherwise they sink into one
+      // dependent chain in front of the PV product).
+      asm volatile("" : "+v"(sum));
+      if constexpr (kExactLse) asm volatile("" : "+v"(xsum));
       __builtin_amdgcn_sched_barrier(0);
     }
     l_run = sum;
+    l_lse = xsum;
   };
   // PV of tile j (8 MFMAs) with the lane maxima of tile j+1's scores, one
   // pair per MFMA; returns the lane maximum (raw scores).
@@ -428,6 +477,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
       if (i + 2 < 8) vf[(i + 2) % 3] = v_read(vt, i + 2);
       acc[i & 3] = T::mfma_32x32x16(vf[i % 3], pk[i >> 2], acc[i & 3]);
       t = fmaxf(fmaxf(t, sn[2 * i]), sn[2 * i + 1]);
+      asm volatile("" : "+v"(t));   // likewise for the running maximum
       __builtin_amdgcn_sched_barrier(0);
     }
     return t;
@@ -488,21 +538,27 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   };
 
   if (ntiles > 0) {
+    // Issue order: every tile the end-of-iteration wait of iteration j must
+    // cover (K(j+2), V(j+1)) has at least 2 * kLoadsPerIter loads issued
+    // after it by then, as in the steady state: iteration 0 needs K(2) and
+    // V(1), followed here by p5, K(3), V(2) (kLoadsPerIter loads) and by
+    // iteration 0's own kLoadsPerIter. The two page-id fetches sit between
+    // the tile loads to make up that count.
     const Pids p0 = fetch_pids(0), p1 = fetch_pids(1), p2 = fetch_pids(2), p3 = fetch_pids(3);
-    pid_k0 = fetch_pids(4);
-    pid_k1 = fetch_pids(5);
     issue(0, p0, kbase, sK0, true);
     issue(0, p0, vbase, sV0, false);
     issue(1, p1, kbase, sK1, true);
+    pid_k0 = fetch_pids(4);
     issue(2, p2, kbase, sK2, true);
     issue(1, p1, vbase, sV1, false);
+    pid_k1 = fetch_pids(5);
     issue(3, p3, kbase, sK3, true);
     issue(2, p2, vbase, sV2, false);
     pid_v = p3;
     if constexpr (MODE == kPagedUniform) grp_v = group_of(3, p3);
-    // K(0), V(0) and K(1) have landed; K(2), V(1), K(3), V(2) may still be
-    // in flight.
-    wait_vm<8>();
+    // K(0), V(0) and K(1) have landed (2 * kLoadsPerIter loads follow K(1));
+    // p4, K(2), V(1), p5, K(3), V(2) may still be in flight.
+    wait_vm<2 * kLoadsPerIter>();
     lds_barrier();
 
     f32x16 sA, sB;
@@ -534,10 +590,27 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   }
 
   // Finalize row lr.
-  const float l_tot = sum_across_halves(l_run);
+  float l_tot = sum_across_halves(l_run);
+  float l_ex = kExactLse ? sum_across_halves(l_lse) : l_tot;
   if (!row_ok) return;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const float lse = l_tot > 0.f ? (m_ref + fast_log2(l_tot)) * kLn2 : neg_inf();
+  float o_scale = 1.f;   // factor on the accumulator besides 1 / l_tot
+  if constexpr (VAR) {
+    // The head's sink (log2 domain) is one more term of both sums, with a
+    // zero value: move the reference to the larger of the two and add it.
+    if (a.var.sinks != nullptr && slot < 0) {
+      const float sink = a.var.sinks[head] * kLog2e;
+      const float m_new = fmaxf(m_ref, sink);
+      if (m_new != neg_inf()) {
+        o_scale = fast_exp2(m_ref - m_new);
+        const float w_sink = fast_exp2(sink - m_new);
+        l_tot = l_tot * o_scale + w_sink;
+        l_ex = l_ex * o_scale + w_sink;
+        m_ref = m_new;
+      }
+    }
+  }
+  const float inv = l_tot > 0.f ? o_scale / l_tot : 0.f;
+  const float lse = l_ex > 0.f ? (m_ref + fast_log2(l_ex)) * kLn2 : neg_inf();
   if (slot < 0) {
     const int64_t orow = static_cast<int64_t>(q0 + qtok) * a.num_qo_heads + head;
     OUT* o = static_cast<OUT*>(a.o) + orow * D;
@@ -566,15 +639,23 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
   }
 }
 
+template <class T, class OUT, bool VAR>
+void launch_prefill_mode(const PrefillArgs& a, PageMode mode, int32_t grid, hipStream_t s) {
+  if (mode == kPagedUniform)
+    hipLaunchKernelGGL((prefill_kernel<T, OUT, kPagedUniform, VAR>), dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<T, OUT, kPagedGeneric, VAR>), dim3(grid), dim3(256), 0, s, a);
+}
+
 template <class T, class OUT>
 hipError_t launch_prefill_t(const PrefillArgs& a, PageMode mode, int32_t grid, hipStream_t s) {
   // The uniform kernel locates pages with shifts: other page sizes use the
   // per-token lookups of the generic kernel.
   if (mode == kPagedUniform && (a.page_size & (a.page_size - 1)) != 0) mode = kPagedGeneric;
-  if (mode == kPagedUniform)
-    hipLaunchKernelGGL((prefill_kernel<T, OUT, kPagedUniform>), dim3(grid), dim3(256), 0, s, a);
+  if (variant_on(a.var))
+    launch_prefill_mode<T, OUT, true>(a, mode, grid, s);
   else
-    hipLaunchKernelGGL((prefill_kernel<T, OUT, kPagedGeneric>), dim3(grid), dim3(256), 0, s, a);
+    launch_prefill_mode<T, OUT, false>(a, mode, grid, s);
   return hipGetLastError();
 }
 
@@ -583,7 +664,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, PageMode mode, int32_t grid, h
 int32_t prefill_occupancy() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&prefill_kernel<BF16, __bf16, kPagedUniform>), 256,
+          &n, reinterpret_cast<const void*>(&prefill_kernel<BF16, __bf16, kPagedUniform, false>), 256,
           0) != hipSuccess)
     return 0;
   return n;

@@ -54,10 +54,14 @@ class pkv_sched(ctypes.Structure):
     _fields_ = [("num_cus", _I32), ("wg_per_cu", _I32), ("min_chunk_tokens", _I32)]
 
 
+class pkv_variant(ctypes.Structure):
+    _fields_ = [("window_left", _I32), ("logits_soft_cap", _F32), ("sinks", _P)]
+
+
 class pkv_plan_part(ctypes.Structure):
     _fields_ = [("num_items", _I32), ("num_groups", _I32), ("chunk_pages", _I32),
                 ("rows_per_tile", _I32), ("num_slots", _I32), ("causal", _I32),
-                ("items_off", _I64), ("groups_off", _I64), ("kv_len_off", _I64),
+                ("window_left", _I32), ("reserved", _I32), ("items_off", _I64), ("groups_off", _I64), ("kv_len_off", _I64),
                 ("part_o_off", _I64), ("part_lse_off", _I64)]
 
 
@@ -83,29 +87,30 @@ _lib_plan_info_size = _sig("pkv_plan_info_size", _SZ, [])
 _lib_default_sched = _sig("pkv_default_sched", _I32, [_I32, ctypes.POINTER(pkv_sched)])
 _lib_default_sched_for = _sig("pkv_default_sched_for", _I32,
                               [_I32, _I32, ctypes.POINTER(pkv_sched)])
+_VARP = ctypes.POINTER(pkv_variant)
 _lib_plan_host = _sig("pkv_plan_host", _I32,
-                      [_I32, _I32P, _I32P, _I32P, _I32, _I32, _I32, _I32, _I32,
+                      [_I32, _I32P, _I32P, _I32P, _I32, _I32, _I32, _I32, _I32, _I32,
                        ctypes.POINTER(pkv_sched), _I32P, _I32, _I32P, _I32, _I32P])
 _lib_decode_plan = _sig("pkv_decode_plan", _I32,
-                        [_I32P, _I32P, _I32, _I32, _I32, _I32, _I32, _I32,
+                        [_I32P, _I32P, _I32, _I32, _I32, _I32, _I32, _I32, _VARP,
                          ctypes.POINTER(pkv_sched), _P, _SZ, _P, _SZ, _P, _SZ, _P,
                          ctypes.POINTER(pkv_plan_info)])
 _lib_decode_run = _sig("pkv_decode_run", _I32,
                        [ctypes.POINTER(pkv_plan_info), _P, ctypes.POINTER(pkv_paged_kv), _P, _P,
-                        _F32, _P, _P, _P])
+                        _F32, _VARP, _P, _P, _P])
 _lib_decode_run_timed = _sig("pkv_decode_run_timed", _I32,
                              [ctypes.POINTER(pkv_plan_info), _P, ctypes.POINTER(pkv_paged_kv), _P,
-                              _P, _F32, _P, _P, _P, _P])
+                              _P, _F32, _VARP, _P, _P, _P, _P])
 _lib_prefill_run_timed = _sig("pkv_prefill_run_timed", _I32,
                               [ctypes.POINTER(pkv_plan_info), _P, ctypes.POINTER(pkv_paged_kv), _P,
-                               _P, _P, _F32, _P, _P, _P, _P])
+                               _P, _P, _F32, _VARP, _P, _P, _P, _P])
 _lib_prefill_plan = _sig("pkv_prefill_plan", _I32,
-                         [_I32P, _I32P, _I32P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                         [_I32P, _I32P, _I32P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _VARP,
                           ctypes.POINTER(pkv_sched), _P, _SZ, _P, _SZ, _P, _SZ, _P,
                           ctypes.POINTER(pkv_plan_info)])
 _lib_prefill_run = _sig("pkv_prefill_run", _I32,
                         [ctypes.POINTER(pkv_plan_info), _P, ctypes.POINTER(pkv_paged_kv), _P, _P,
-                         _P, _F32, _P, _P, _P])
+                         _P, _F32, _VARP, _P, _P, _P])
 _lib_single_decode = _sig("pkv_single_decode", _I32,
                           [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _F32,
                            ctypes.POINTER(pkv_sched), _P, _SZ, ctypes.POINTER(_I64), _P, _P, _P])
@@ -286,7 +291,7 @@ def pkv_default_sched_for(kind: int, device: int = 0) -> pkv_sched:
 
 
 def pkv_plan_host(kind, qo_indptr, kv_indptr, last_page_len, num_qo_heads, num_kv_heads,
-                  page_size, causal, sched):
+                  page_size, causal, sched, window_left=-1):
     """Host-only plan: returns (items [n, 8], groups [m, 8], counts [4]) as int32 arrays."""
     kvp, lpl = _host_i32(kv_indptr), _host_i32(last_page_len)
     qop = None if qo_indptr is None else _host_i32(qo_indptr)
@@ -295,7 +300,8 @@ def pkv_plan_host(kind, qo_indptr, kv_indptr, last_page_len, num_qo_heads, num_k
     s = sched if isinstance(sched, pkv_sched) else pkv_sched(*sched)
     args = lambda it, ic, gr, gc: _lib_plan_host(  # noqa: E731
         kind, None if qop is None else _i32p(qop), _i32p(kvp), _i32p(lpl), batch, num_qo_heads,
-        num_kv_heads, page_size, causal, ctypes.byref(s), it, ic, gr, gc, _i32p(counts))
+        num_kv_heads, page_size, causal, int(window_left), ctypes.byref(s), it, ic, gr, gc,
+        _i32p(counts))
     st = args(None, 0, None, 0)
     if st not in (PKV_OK, PKV_ERR_WORKSPACE_TOO_SMALL):
         _check(st, "pkv_plan_host")
@@ -305,20 +311,34 @@ def pkv_plan_host(kind, qo_indptr, kv_indptr, last_page_len, num_qo_heads, num_k
     return items[:counts[0]], groups[:counts[1]], counts.copy()
 
 
+def _variant(window_left=-1, logits_soft_cap=0.0, sinks=None):
+    """A pkv_variant (by reference) for a call, or None when every variant is off.
+    ``sinks`` is a float32 device tensor [num_qo_heads] or None."""
+    if int(window_left) == -1 and float(logits_soft_cap) == 0.0 and sinks is None:
+        return None
+    if sinks is not None and (sinks.dtype != torch.float32 or not sinks.is_contiguous()):
+        raise ValueError("sinks must be a contiguous float32 tensor [num_qo_heads]")
+    return ctypes.byref(pkv_variant(int(window_left), float(logits_soft_cap),
+                                    None if sinks is None else sinks.data_ptr()))
+
+
 def pkv_decode_plan(kv_indptr, last_page_len, num_qo_heads, num_kv_heads, head_dim, page_size,
-                    dtype, workspace: Workspace, sched=None, stream=None) -> pkv_plan_info:
+                    dtype, workspace: Workspace, sched=None, stream=None,
+                    window_left=-1) -> pkv_plan_info:
     kvp, lpl = _host_i32(kv_indptr), _host_i32(last_page_len)
     code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    var = _variant(window_left)
 
     def call(ws, info):
         return _lib_decode_plan(_i32p(kvp), _i32p(lpl), len(kvp) - 1, num_qo_heads, num_kv_heads,
-                                head_dim, page_size, code, _sched_arg(sched), *ws.args(),
+                                head_dim, page_size, code, var, _sched_arg(sched), *ws.args(),
                                 _stream(stream), ctypes.byref(info))
     return _plan_with_growth(call, workspace, "pkv_decode_plan")
 
 
 def pkv_decode_run(plan: pkv_plan_info, q, k_cache, v_cache, kv_indptr_d, kv_indices_d,
-                   sm_scale: float, o=None, lse=None, stream=None):
+                   sm_scale: float, o=None, lse=None, stream=None, window_left=-1,
+                   logits_soft_cap=0.0, sinks=None):
     """q [batch, Hq, D] -> (o like q, lse [batch, Hq] float32)."""
     kv = paged_kv(k_cache, v_cache)
     q = q.contiguous()
@@ -326,12 +346,14 @@ def pkv_decode_run(plan: pkv_plan_info, q, k_cache, v_cache, kv_indptr_d, kv_ind
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if lse is None else lse
     _check(_lib_decode_run(ctypes.byref(plan), q.data_ptr(), ctypes.byref(kv),
                            kv_indptr_d.data_ptr(), kv_indices_d.data_ptr(), float(sm_scale),
-                           o.data_ptr(), _ptr(lse), _stream(stream)), "pkv_decode_run")
+                           _variant(window_left, logits_soft_cap, sinks), o.data_ptr(),
+                           _ptr(lse), _stream(stream)), "pkv_decode_run")
     return o, lse
 
 
 def pkv_decode_run_timed(plan: pkv_plan_info, q, k_cache, v_cache, kv_indptr_d, kv_indices_d,
-                         sm_scale: float, attention_done, o=None, lse=None, stream=None):
+                         sm_scale: float, attention_done, o=None, lse=None, stream=None,
+                         window_left=-1, logits_soft_cap=0.0, sinks=None):
     """pkv_decode_run that records the torch.cuda.Event `attention_done` after the
     attention kernel (before the merge)."""
     kv = paged_kv(k_cache, v_cache)
@@ -340,27 +362,30 @@ def pkv_decode_run_timed(plan: pkv_plan_info, q, k_cache, v_cache, kv_indptr_d, 
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if lse is None else lse
     _check(_lib_decode_run_timed(ctypes.byref(plan), q.data_ptr(), ctypes.byref(kv),
                                  kv_indptr_d.data_ptr(), kv_indices_d.data_ptr(), float(sm_scale),
-                                 o.data_ptr(), _ptr(lse), _stream(stream),
-                                 _event(attention_done)), "pkv_decode_run_timed")
+                                 _variant(window_left, logits_soft_cap, sinks), o.data_ptr(),
+                                 _ptr(lse), _stream(stream), _event(attention_done)),
+           "pkv_decode_run_timed")
     return o, lse
 
 
 def pkv_prefill_plan(qo_indptr, kv_indptr, last_page_len, num_qo_heads, num_kv_heads, head_dim,
                      page_size, dtype, causal, workspace: Workspace, sched=None,
-                     stream=None) -> pkv_plan_info:
+                     stream=None, window_left=-1) -> pkv_plan_info:
     qop, kvp, lpl = _host_i32(qo_indptr), _host_i32(kv_indptr), _host_i32(last_page_len)
     code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+    var = _variant(window_left)
 
     def call(ws, info):
         return _lib_prefill_plan(_i32p(qop), _i32p(kvp), _i32p(lpl), len(kvp) - 1, num_qo_heads,
-                                 num_kv_heads, head_dim, page_size, code, int(causal),
+                                 num_kv_heads, head_dim, page_size, code, int(causal), var,
                                  _sched_arg(sched), *ws.args(), _stream(stream),
                                  ctypes.byref(info))
     return _plan_with_growth(call, workspace, "pkv_prefill_plan")
 
 
 def pkv_prefill_run(plan: pkv_plan_info, q, k_cache, v_cache, qo_indptr_d, kv_indptr_d,
-                    kv_indices_d, sm_scale: float, o=None, lse=None, stream=None):
+                    kv_indices_d, sm_scale: float, o=None, lse=None, stream=None,
+                    window_left=-1, logits_soft_cap=0.0, sinks=None):
     """q [total_qo, Hq, D] -> (o like q, lse [total_qo, Hq] float32)."""
     kv = paged_kv(k_cache, v_cache)
     q = q.contiguous()
@@ -368,14 +393,15 @@ def pkv_prefill_run(plan: pkv_plan_info, q, k_cache, v_cache, qo_indptr_d, kv_in
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if lse is None else lse
     _check(_lib_prefill_run(ctypes.byref(plan), q.data_ptr(), ctypes.byref(kv),
                             qo_indptr_d.data_ptr(), kv_indptr_d.data_ptr(),
-                            kv_indices_d.data_ptr(), float(sm_scale), o.data_ptr(), _ptr(lse),
-                            _stream(stream)), "pkv_prefill_run")
+                            kv_indices_d.data_ptr(), float(sm_scale),
+                            _variant(window_left, logits_soft_cap, sinks), o.data_ptr(),
+                            _ptr(lse), _stream(stream)), "pkv_prefill_run")
     return o, lse
 
 
 def pkv_prefill_run_timed(plan: pkv_plan_info, q, k_cache, v_cache, qo_indptr_d, kv_indptr_d,
                           kv_indices_d, sm_scale: float, attention_done, o=None, lse=None,
-                          stream=None):
+                          stream=None, window_left=-1, logits_soft_cap=0.0, sinks=None):
     """pkv_prefill_run that records `attention_done` after the attention kernel."""
     kv = paged_kv(k_cache, v_cache)
     q = q.contiguous()
@@ -383,7 +409,8 @@ def pkv_prefill_run_timed(plan: pkv_plan_info, q, k_cache, v_cache, qo_indptr_d,
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if lse is None else lse
     _check(_lib_prefill_run_timed(ctypes.byref(plan), q.data_ptr(), ctypes.byref(kv),
                                   qo_indptr_d.data_ptr(), kv_indptr_d.data_ptr(),
-                                  kv_indices_d.data_ptr(), float(sm_scale), o.data_ptr(),
+                                  kv_indices_d.data_ptr(), float(sm_scale),
+                                  _variant(window_left, logits_soft_cap, sinks), o.data_ptr(),
                                   _ptr(lse), _stream(stream), _event(attention_done)),
            "pkv_prefill_run_timed")
     return o, lse

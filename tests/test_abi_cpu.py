@@ -27,21 +27,24 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_struct_size(lib):
-    assert lib.pkv_abi_version() == 1
+    assert lib.pkv_abi_version() == 2
     assert lib.pkv_plan_info_size() == ctypes.sizeof(lib.pkv_plan_info)
 
 
 SCHED = (256, 4, 256)
 
 
-def _decode_plan(lib, indptr, lpl, hq=32, hkv=8, head_dim=128, P=16, dtype=0, sched=SCHED):
+def _decode_plan(lib, indptr, lpl, hq=32, hkv=8, head_dim=128, P=16, dtype=0, sched=SCHED,
+                 variant=None):
     indptr = np.asarray(indptr, np.int32)
     lpl = np.asarray(lpl, np.int32)
     info = lib.pkv_plan_info()
     s = lib.pkv_sched(*sched)
     st = lib._lib_decode_plan(lib._i32p(indptr), lib._i32p(lpl), len(indptr) - 1, hq, hkv,
-                              head_dim, P, dtype, ctypes.byref(s), None, 0, None, 0, None, 0,
-                              None, ctypes.byref(info))
+                              head_dim, P, dtype,
+                              None if variant is None else ctypes.byref(variant),
+                              ctypes.byref(s), None, 0, None, 0, None, 0, None,
+                              ctypes.byref(info))
     return st, info
 
 
@@ -84,12 +87,12 @@ def test_prefill_plan_rejects_bad_qo_indptr(lib):
     info = lib.pkv_plan_info()
     s = lib.pkv_sched(*SCHED)
     st = lib._lib_prefill_plan(lib._i32p(qo), lib._i32p(kv), lib._i32p(lpl), 2, 32, 8, 128, 16, 1,
-                               1, ctypes.byref(s), None, 0, None, 0, None, 0, None,
+                               1, None, ctypes.byref(s), None, 0, None, 0, None, 0, None,
                                ctypes.byref(info))
     assert st == lib.PKV_ERR_INVALID_ARG
     st = lib._lib_prefill_plan(lib._i32p(np.array([0, 1, 3], np.int32)), lib._i32p(kv),
-                               lib._i32p(lpl), 2, 32, 8, 128, 16, 1, 2, ctypes.byref(s), None, 0,
-                               None, 0, None, 0, None, ctypes.byref(info))
+                               lib._i32p(lpl), 2, 32, 8, 128, 16, 1, 2, None, ctypes.byref(s),
+                               None, 0, None, 0, None, 0, None, ctypes.byref(info))
     assert st == lib.PKV_ERR_INVALID_ARG     # causal must be 0 or 1
 
 
@@ -97,29 +100,76 @@ def test_run_rejects_foreign_or_mismatched_plans(lib):
     bogus = lib.pkv_plan_info()
     kv = lib.pkv_paged_kv()
     st = lib._lib_decode_run(ctypes.byref(bogus), None, ctypes.byref(kv), None, None, 1.0, None,
-                             None, None)
+                             None, None, None)
     assert st == lib.PKV_ERR_PLAN_MISMATCH
     # a well-formed plan header with a different page size than the KV description
     st, info = _decode_plan(lib, [0, 1], [1])
     assert st == lib.PKV_ERR_WORKSPACE_TOO_SMALL   # no workspaces given: header still filled
     info.magic = 0x31564B50
-    info.abi_version = 1
+    info.abi_version = 2
     info.kind = lib.PKV_KIND_DECODE
     info.page_size, info.num_kv_heads, info.head_dim, info.dtype = 16, 8, 128, 0
     kv.k = kv.v = 1 << 20
     kv.page_size, kv.num_kv_heads, kv.head_dim, kv.dtype = 32, 8, 128, 0
     st = lib._lib_decode_run(ctypes.byref(info), None, ctypes.byref(kv), None, None, 1.0, None,
-                             None, None)
+                             None, None, None)
     assert st == lib.PKV_ERR_PLAN_MISMATCH
     kv.page_size = 16
     kv.token_stride = 12                          # not a multiple of 8 elements
     st = lib._lib_decode_run(ctypes.byref(info), None, ctypes.byref(kv), None, None, 1.0, None,
-                             None, None)
+                             None, None, None)
     assert st == lib.PKV_ERR_INVALID_ARG
     info.kind = lib.PKV_KIND_PREFILL
     st = lib._lib_decode_run(ctypes.byref(info), None, ctypes.byref(kv), None, None, 1.0, None,
-                             None, None)
+                             None, None, None)
     assert st == lib.PKV_ERR_PLAN_MISMATCH
+
+
+def _fake_decode_plan(lib, window_left=-1):
+    """A well-formed decode plan header (no workspaces) and a matching KV view."""
+    st, info = _decode_plan(lib, [0, 1], [1], variant=lib.pkv_variant(window_left, 0.0, None))
+    assert st == lib.PKV_ERR_WORKSPACE_TOO_SMALL
+    info.magic = 0x31564B50
+    info.abi_version = 2
+    info.kind = lib.PKV_KIND_DECODE
+    info.page_size, info.num_kv_heads, info.head_dim, info.dtype = 16, 8, 128, 0
+    kv = lib.pkv_paged_kv()
+    kv.k = kv.v = 1 << 20
+    kv.page_size, kv.num_kv_heads, kv.head_dim, kv.dtype = 16, 8, 128, 0
+    kv.page_stride, kv.token_stride, kv.head_stride = 16 * 8 * 128, 8 * 128, 128
+    return info, kv
+
+
+def _run(lib, info, kv, variant):
+    return lib._lib_decode_run(ctypes.byref(info), None, ctypes.byref(kv), None, None, 0.125,
+                               None if variant is None else ctypes.byref(variant), None, None,
+                               None)
+
+
+def test_variant_validation(lib):
+    """Plan: window_left < -1 is invalid; the plan records its window. Run: the window
+    must equal the plan's; the soft cap must be finite and >= 0; sinks 4-byte aligned.
+    Every check happens before any launch (q is NULL, so a valid variant then fails
+    on the NULL q with INVALID_ARG, not with a GPU call)."""
+    st, _ = _decode_plan(lib, [0, 1], [1], variant=lib.pkv_variant(-2, 0.0, None))
+    assert st == lib.PKV_ERR_INVALID_ARG and "window_left" in lib.pkv_last_error()
+    info, kv = _fake_decode_plan(lib, window_left=64)
+    assert info.part[0].window_left == 64
+    assert _run(lib, info, kv, None) == lib.PKV_ERR_PLAN_MISMATCH
+    assert _run(lib, info, kv, lib.pkv_variant(63, 0.0, None)) == lib.PKV_ERR_PLAN_MISMATCH
+    assert _run(lib, info, kv, lib.pkv_variant(64, -1.0, None)) == lib.PKV_ERR_INVALID_ARG
+    assert _run(lib, info, kv, lib.pkv_variant(64, float("nan"), None)) == lib.PKV_ERR_INVALID_ARG
+    assert _run(lib, info, kv, lib.pkv_variant(64, float("inf"), None)) == lib.PKV_ERR_INVALID_ARG
+    assert _run(lib, info, kv, lib.pkv_variant(64, 1e-38, None)) == lib.PKV_ERR_INVALID_ARG
+    assert _run(lib, info, kv, lib.pkv_variant(64, 30.0, (1 << 20) + 2)) == lib.PKV_ERR_INVALID_ARG
+    assert "sinks" in lib.pkv_last_error()
+    st = _run(lib, info, kv, lib.pkv_variant(64, 30.0, 1 << 20))
+    assert st == lib.PKV_ERR_INVALID_ARG and "NULL" in lib.pkv_last_error()
+    info, kv = _fake_decode_plan(lib)
+    assert info.part[0].window_left == -1
+    assert _run(lib, info, kv, lib.pkv_variant(5, 0.0, None)) == lib.PKV_ERR_PLAN_MISMATCH
+    st = _run(lib, info, kv, None)
+    assert st == lib.PKV_ERR_INVALID_ARG and "NULL" in lib.pkv_last_error()
 
 
 def test_merge_rejects_bad_arguments(lib):
@@ -164,9 +214,9 @@ def test_runs_reject_bad_scales(lib):
     info = lib.pkv_plan_info()
     for scale in (0.0, -0.5, float("inf"), float("nan")):
         assert lib._lib_decode_run(ctypes.byref(info), None, ctypes.byref(kv), None, None, scale,
-                                   None, None, None) == lib.PKV_ERR_INVALID_ARG
+                                   None, None, None, None) == lib.PKV_ERR_INVALID_ARG
         assert lib._lib_prefill_run(ctypes.byref(info), None, ctypes.byref(kv), None, None, None,
-                                    scale, None, None, None) == lib.PKV_ERR_INVALID_ARG
+                                    scale, None, None, None, None) == lib.PKV_ERR_INVALID_ARG
 
 
 def test_append_validates_before_any_launch(lib):

@@ -215,3 +215,28 @@ def test_window_off_is_the_plain_rule():
         a = plan_spec(qo, kv, P, 2, G, 128, True, 256, 4, 256)
         b = plan_spec(qo, kv, P, 2, G, 128, True, 256, 4, 256, window_left=-1)
         assert a.items == b.items and a.merge_groups == b.merge_groups
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_cpp_planner_equals_spec_with_window(lib, seed):
+    rng = np.random.default_rng(2000 + seed)
+    B, P, G, qo, kv, W = _window_case(rng)
+    decode = seed % 2 == 1
+    if decode:
+        qo = np.ones(B, dtype=np.int64)
+    causal = decode or seed % 4 != 0
+    R = G if decode else 128
+    sched = SCHEDS[seed % len(SCHEDS)]
+    n = -(-kv // P)
+    indptr = np.zeros(B + 1, dtype=np.int32)
+    indptr[1:] = np.cumsum(n)
+    lpl = np.where(n > 0, kv - (n - 1) * P, 0).astype(np.int32)
+    qo_indptr = np.zeros(B + 1, dtype=np.int32)
+    qo_indptr[1:] = np.cumsum(qo)
+    spec = plan_spec(qo, kv, P, 2, G, R, causal, *sched, window_left=W)
+    items, groups, counts = lib.pkv_plan_host(
+        lib.PKV_KIND_DECODE if decode else lib.PKV_KIND_PREFILL, None if decode else qo_indptr,
+        indptr, lpl, G * 2, 2, P, int(causal), sched, window_left=W)
+    assert counts[2] == spec.chunk_pages and counts[3] == spec.num_slots
+    assert [tuple(r) for r in items.tolist()] == [tuple(r) for r in spec.items]
+    assert [tuple(r[:5]) for r in groups.tolist()] == [tuple(g) for g in spec.merge_groups]
