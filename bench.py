@@ -42,6 +42,7 @@ def log(*a):
 # Sources the decode kernel is compiled from; a traffic figure in profiles/ is
 # used only while their hash matches the one recorded next to it.
 DECODE_SOURCES = ["paged_kv_cache_173_amd/csrc/decode.hip",
+                  "paged_kv_cache_173_amd/csrc/decode_item.h",
                   "paged_kv_cache_173_amd/csrc/device_common.h",
                   "paged_kv_cache_173_amd/csrc/kernels.h"]
 TRAFFIC_PROFILE = "profiles/decode_kernel_batch64_fp16_hbm_traffic.md"
@@ -84,16 +85,19 @@ def decode_bytes(kv_lens, Hkv, D, elem, B, Hq):
     return kv + B * Hq * D * elem * 2 + B * Hq * 4
 
 
-def prefill_flops(qo_lens, kv_lens, Hq, D, causal):
-    """4 * D * Hq * (number of visible (query, key) pairs)."""
+def prefill_flops(qo_lens, kv_lens, Hq, D, causal, window_left=-1):
+    """4 * D * Hq * (number of visible (query, key) pairs); with a sliding window the
+    query at position p sees keys max(0, p - W) .. p (causal) or .. L - 1."""
     pairs = 0
     for Q, L in zip(qo_lens, kv_lens):
         Q, L = int(Q), int(L)
-        if causal:
-            pre = L - Q
-            pairs += Q * pre + Q * (Q + 1) // 2
-        else:
-            pairs += Q * L
+        if window_left < 0:
+            pairs += Q * (L - Q) + Q * (Q + 1) // 2 if causal else Q * L
+            continue
+        p = np.arange(Q, dtype=np.int64) + (L - Q)
+        hi = np.minimum(p, L - 1) if causal else np.full(Q, L - 1, np.int64)
+        lo = np.maximum(p - window_left, 0)
+        pairs += int(np.sum(np.maximum(hi - lo + 1, 0)))
     return 4.0 * D * Hq * pairs
 
 
@@ -132,6 +136,24 @@ class Runner:
             self._plan()
             self.plan_us = (time.perf_counter() - t0) * 1e6
             return
+        if w.kind == "pod":
+            wp, wd = w.prefill, w.decode
+            self.k, self.v = dev(wp.kv.k_cache), dev(wp.kv.v_cache)
+            self.q_p, self.q_d = dev(wp.q), dev(wd.q)
+            self.qo = dev_i32(wp.qo_indptr)
+            self.ip, self.ix = dev_i32(wp.kv.kv_indptr), dev_i32(wp.kv.kv_indices)
+            self.dp, self.dx = dev_i32(wd.kv.kv_indptr), dev_i32(wd.kv.kv_indices)
+            self.o_p, self.o_d = torch.empty_like(self.q_p), torch.empty_like(self.q_d)
+            self.l_p = torch.empty(self.q_p.shape[:2], dtype=torch.float32, device="cuda")
+            self.l_d = torch.empty(self.q_d.shape[:2], dtype=torch.float32, device="cuda")
+            self.ws, self.ws_p, self.ws_d = pkv.Workspace(), pkv.Workspace(), pkv.Workspace()
+            self.dt = dt
+            self.sequential = False     # True: the same parts as separate prefill + decode runs
+            self._plan()
+            t0 = time.perf_counter()
+            self._plan()
+            self.plan_us = (time.perf_counter() - t0) * 1e6
+            return
         if w.kind == "append":
             self.ak, self.av = dev(w.append_k), dev(w.append_v)
             self.k, self.v = dev(w.kv.k_cache), dev(w.kv.v_cache)
@@ -144,6 +166,11 @@ class Runner:
             return
         self.q = dev(w.q)
         self.ws = pkv.Workspace()
+        var = w.meta.get("variant") or {}
+        self.window_left = int(var.get("window_left", -1))
+        self.soft_cap = float(var.get("logits_soft_cap", 0.0))
+        self.sinks = (torch.from_numpy(np.asarray(var["sinks"], np.float32)).to("cuda")
+                      if var.get("sinks") is not None else None)
         if w.kind == "single_decode":
             self.k, self.v = dev(w.k), dev(w.v)
             self.o = torch.empty_like(self.q)
@@ -166,7 +193,17 @@ class Runner:
 
     def _plan(self):
         w, pkv, torch, dt = self.w, self.pkv, self.torch, self.dt
-        if w.kind == "block_sparse":
+        if w.kind == "pod":
+            wp, wd = w.prefill, w.decode
+            Hq, Hkv, P = wp.num_qo_heads, wp.num_kv_heads, wp.kv.page_size
+            self.plan = pkv.pkv_pod_plan(wp.qo_indptr, wp.kv.kv_indptr, wp.kv.last_page_len,
+                                         wp.causal, wd.kv.kv_indptr, wd.kv.last_page_len, Hq, Hkv,
+                                         wp.head_dim, P, dt, self.ws)
+            self.plan_p = pkv.pkv_prefill_plan(wp.qo_indptr, wp.kv.kv_indptr, wp.kv.last_page_len,
+                                               Hq, Hkv, wp.head_dim, P, dt, wp.causal, self.ws_p)
+            self.plan_d = pkv.pkv_decode_plan(wd.kv.kv_indptr, wd.kv.last_page_len, Hq, Hkv,
+                                              wd.head_dim, P, dt, self.ws_d)
+        elif w.kind == "block_sparse":
             self.plan = pkv.pkv_block_sparse_plan(w.bsr_indptr, w.bsr_indices, w.q.shape[0],
                                                   w.k.shape[0], w.row_block, w.col_block,
                                                   w.num_qo_heads, w.num_kv_heads, w.head_dim, dt,
@@ -182,11 +219,12 @@ class Runner:
         elif w.kind == "decode":
             self.plan = pkv.pkv_decode_plan(w.kv.kv_indptr, w.kv.last_page_len, w.num_qo_heads,
                                             w.num_kv_heads, w.head_dim, w.kv.page_size, dt,
-                                            self.ws)
+                                            self.ws, window_left=self.window_left)
         elif w.kind == "prefill":
             self.plan = pkv.pkv_prefill_plan(w.qo_indptr, w.kv.kv_indptr, w.kv.last_page_len,
                                              w.num_qo_heads, w.num_kv_heads, w.head_dim,
-                                             w.kv.page_size, dt, w.causal, self.ws)
+                                             w.kv.page_size, dt, w.causal, self.ws,
+                                             window_left=self.window_left)
         else:
             self.plan = pkv.pkv_cascade_plan(len(w.prefix_indices), w.prefix_last_page_len,
                                              w.kv.kv_indptr, w.kv.last_page_len, w.num_qo_heads,
@@ -197,7 +235,16 @@ class Runner:
         """One run; `attention_done` (decode / prefill) is recorded after the attention
         kernel, before the merge of split chunks."""
         p, w = self.pkv, self.w
-        if w.kind == "block_sparse":
+        if w.kind == "pod" and self.sequential:
+            p.pkv_prefill_run(self.plan_p, self.q_p, self.k, self.v, self.qo, self.ip, self.ix,
+                              w.prefill.sm_scale, o=self.o_p, lse=self.l_p)
+            p.pkv_decode_run_timed(self.plan_d, self.q_d, self.k, self.v, self.dp, self.dx,
+                                   w.decode.sm_scale, attention_done, o=self.o_d, lse=self.l_d)
+        elif w.kind == "pod":
+            p.pkv_pod_run(self.plan, self.k, self.v, self.q_p, self.qo, self.ip, self.ix, self.q_d,
+                          self.dp, self.dx, w.prefill.sm_scale, o_p=self.o_p, lse_p=self.l_p,
+                          o_d=self.o_d, lse_d=self.l_d, attention_done=attention_done)
+        elif w.kind == "block_sparse":
             p.pkv_block_sparse_run(self.plan, self.q, self.k, self.v, self.ip, self.ix,
                                    w.sm_scale, o=self.o, lse=self.lse)
         elif w.kind == "append":
@@ -209,11 +256,13 @@ class Runner:
         elif w.kind == "decode":
             p.pkv_decode_run_timed(self.plan, self.q, self.k, self.v, self.kv_indptr,
                                    self.kv_indices, w.sm_scale, attention_done, o=self.o,
-                                   lse=self.lse)
+                                   lse=self.lse, window_left=self.window_left,
+                                   logits_soft_cap=self.soft_cap, sinks=self.sinks)
         elif w.kind == "prefill":
             p.pkv_prefill_run_timed(self.plan, self.q, self.k, self.v, self.qo_indptr,
                                     self.kv_indptr, self.kv_indices, w.sm_scale, attention_done,
-                                    o=self.o, lse=self.lse)
+                                    o=self.o, lse=self.lse, window_left=self.window_left,
+                                    logits_soft_cap=self.soft_cap, sinks=self.sinks)
         else:
             p.pkv_cascade_run(self.plan, self.q, self.k, self.v, self.prefix, self.kv_indptr,
                               self.kv_indices, w.sm_scale, o=self.o, lse=self.lse)
@@ -221,6 +270,14 @@ class Runner:
     def work(self):
         """(algorithmic bytes, algorithmic flops, tokens) of one step."""
         w = self.w
+        if w.kind == "pod":
+            wp, wd = w.prefill, w.decode
+            fp = prefill_flops(wp.meta["qo_lens"], wp.kv.kv_lens, wp.num_qo_heads, wp.head_dim,
+                               wp.causal)
+            B = len(wd.kv.kv_lens)
+            bd = decode_bytes(wd.kv.kv_lens, wd.num_kv_heads, wd.head_dim, 2, B, wd.num_qo_heads)
+            fd = 4.0 * wd.num_qo_heads * wd.head_dim * float(np.sum(wd.kv.kv_lens))
+            return prefill_bytes(wp) + bd, fp + fd, int(np.sum(wp.meta["qo_lens"])) + B
         if w.kind == "block_sparse":
             R, C, Nq, Nkv = w.row_block, w.col_block, w.q.shape[0], w.k.shape[0]
             pairs = 0
@@ -242,11 +299,14 @@ class Runner:
             return b, 4.0 * w.num_qo_heads * w.head_dim * L, 1
         if w.kind == "decode":
             B = len(w.kv.kv_lens)
-            b = decode_bytes(w.kv.kv_lens, w.num_kv_heads, w.head_dim, 2, B, w.num_qo_heads)
-            return b, 4.0 * w.num_qo_heads * w.head_dim * float(np.sum(w.kv.kv_lens)), B
+            # with a sliding window a request needs only its last W + 1 keys
+            seen = (w.kv.kv_lens if self.window_left < 0 else
+                    np.minimum(w.kv.kv_lens, self.window_left + 1))
+            b = decode_bytes(seen, w.num_kv_heads, w.head_dim, 2, B, w.num_qo_heads)
+            return b, 4.0 * w.num_qo_heads * w.head_dim * float(np.sum(seen)), B
         if w.kind == "prefill":
             f = prefill_flops(w.meta["qo_lens"], w.kv.kv_lens, w.num_qo_heads, w.head_dim,
-                              w.causal)
+                              w.causal, self.window_left)
             return prefill_bytes(w), f, int(np.sum(w.meta["qo_lens"]))
         B = len(w.kv.kv_lens)
         pre = w.meta["prefix_len"]
@@ -263,7 +323,7 @@ def time_steps(torch, runner, steps, warmup, flush):
     def evict():
         return flush.view(torch.int64).sum()
 
-    timed_kernel = runner.w.kind in ("decode", "prefill")
+    timed_kernel = runner.w.kind in ("decode", "prefill", "pod")
     for _ in range(warmup):
         evict()
         runner.step(torch.cuda.Event(enable_timing=True) if timed_kernel else None)
@@ -322,7 +382,29 @@ def cpu_baseline(w, min_s=10.0, max_s=30.0):
 
 
 WORKLOADS = {"single": 0, "decode": 1, "prefill": 2, "cascade": 3, "long": 4, "append": 5,
-             "block_sparse": 6}
+             "block_sparse": 6, "pod": 7, "decode_variants": 8, "prefill_variants": 9}
+
+
+def with_variants(w, window_left, soft_cap, seed):
+    """The workload with a sliding window, a logit soft cap and seeded N(0, 2) sinks."""
+    rng = np.random.default_rng(seed)
+    w.meta["variant"] = {"window_left": window_left, "logits_soft_cap": soft_cap,
+                         "sinks": (rng.standard_normal(w.num_qo_heads) * 2).astype(np.float32)}
+    return w
+
+
+def make_workload(name, wl):
+    if name == "append":
+        return wl.append_kv()
+    if name == "block_sparse":
+        return wl.block_sparse()
+    if name == "pod":
+        return wl.pod()
+    if name == "decode_variants":
+        return with_variants(wl.FULL[1](), 1023, 30.0, 173008)
+    if name == "prefill_variants":
+        return with_variants(wl.FULL[2](), 1023, 50.0, 173009)
+    return wl.FULL[WORKLOADS[name]]()
 
 
 def main():
@@ -347,13 +429,13 @@ def main():
     log(f"[bench] generating workload {args.workload}")
     flush = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
     names = [args.workload] + ([n for n in ("single", "decode", "prefill", "cascade", "long",
-                                            "append", "block_sparse")
+                                            "append", "block_sparse", "pod", "decode_variants",
+                                            "prefill_variants")
                                  if n != args.workload] if args.all else [])
     results = {}
     headline = None
     for name in names:
-        w = (wl.append_kv() if name == "append" else
-             wl.block_sparse() if name == "block_sparse" else wl.FULL[WORKLOADS[name]]())
+        w = make_workload(name, wl)
         r = Runner(name, w, pkv, torch)
         log(f"[bench] {name}: planned in {r.plan_us:.0f} us; timing {args.steps} steps")
         mean_ms, med_ms, kern_ms, wall = time_steps(torch, r, args.steps, args.warmup, flush)
@@ -368,6 +450,15 @@ def main():
         kern_ms = kern_ms if kern_ms else mean_ms
         res["kernel_GBps"] = nbytes / (kern_ms * 1e-3) / 1e9
         res["kernel_TFLOPs"] = flops / (kern_ms * 1e-3) / 1e12
+        if name == "pod":
+            # the same two parts as separate prefill and decode runs, timed the same way
+            r.sequential = True
+            s_mean, s_med, s_kern, _ = time_steps(torch, r, args.steps, args.warmup, flush)
+            r.sequential = False
+            res["sequential_ms_per_step"] = s_mean
+            res["pod_speedup"] = s_mean / mean_ms
+            log(f"[bench] pod: separate prefill + decode runs {s_mean * 1e3:.1f} us/step; "
+                f"one mixed launch {mean_ms * 1e3:.1f} us/step ({s_mean / mean_ms:.3f}x)")
         log(f"[bench] {name}: {mean_ms * 1e3:.1f} us/step, {res['GBps']:.0f} GB/s "
             f"({100 * res['hbm_frac']:.1f}% HBM), {res['TFLOPs']:.1f} TFLOP/s; attention kernel "
             f"{kern_ms * 1e3:.1f} us: {res['kernel_GBps']:.0f} GB/s, "
@@ -380,7 +471,7 @@ def main():
             torch.cuda.empty_cache()
 
     name, w, r, res = headline
-    prefill_like = name in ("prefill", "block_sparse")
+    prefill_like = name in ("prefill", "block_sparse", "pod", "prefill_variants")
     line = {
         "metric": "paged decode HBM GB/s (% peak); prefill TFLOPS (% MFMA peak); tokens/s",
         "value": res["TFLOPs"] if prefill_like else res["GBps"],
@@ -402,6 +493,13 @@ def main():
                       "cache, 8 KV heads, P=16, bf16",
             "block_sparse": "block-sparse attention, 8192 x 8192 tokens, 64 x 64 blocks, "
                             "density 0.25 + diagonal, 32/8 heads, bf16",
+            "pod": "mixed batch in one launch: the causal prefill workload's 16 requests and "
+                   "64 decode requests with kv_len U[512,4096], 32/8 heads, P=16, bf16",
+            "decode_variants": "batch paged decode, 64 requests, kv_len U[512,4096], 32/8 heads, "
+                               "P=16, fp16, sliding window 1023, logit soft cap 30, sinks",
+            "prefill_variants": "batch paged causal prefill, 16 requests, qo U[128,1024] after "
+                                "prefix U[0,2048], 32/8 heads, P=16, bf16, sliding window 1023, "
+                                "logit soft cap 50, sinks",
         }[name], "head_dim": 128, "tokens_per_step": r.work()[2],
             "tokens_per_s": res["tokens_per_s"], "plan_us": res["plan_us"]},
         # the dominant kernel (the attention kernel, timed alone with events)
@@ -418,7 +516,7 @@ def main():
     }
     if len(results) > 1:
         line["workloads"] = results
-    if not args.no_cpu_baseline and w.kind == "decode":
+    if not args.no_cpu_baseline and name == "decode":
         log("[bench] timing the CPU oracle on a bounded sample")
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

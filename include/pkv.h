@@ -72,7 +72,13 @@ typedef int32_t pkv_dtype;
 enum { PKV_F16 = 0, PKV_BF16 = 1, PKV_F32 = 2 };
 
 typedef int32_t pkv_kind;
-enum { PKV_KIND_DECODE = 1, PKV_KIND_PREFILL = 2, PKV_KIND_CASCADE = 3, PKV_KIND_BLOCK_SPARSE = 4 };
+enum {
+  PKV_KIND_DECODE = 1,
+  PKV_KIND_PREFILL = 2,
+  PKV_KIND_CASCADE = 3,
+  PKV_KIND_BLOCK_SPARSE = 4,
+  PKV_KIND_POD = 5
+};
 
 /* A paged K/V cache. k and v are separate device bases with one set of
  * strides (in elements), which also covers an interleaved [pages, 2, P, H, D]
@@ -167,7 +173,11 @@ typedef struct pkv_plan_info {
   int64_t int_ws_required;   /* bytes (also set on WORKSPACE_TOO_SMALL)      */
   int64_t float_ws_required; /* bytes (also set on WORKSPACE_TOO_SMALL)      */
   int64_t cascade_state_off; /* cascade: float ws offset of the two fp32 states */
-  pkv_plan_part part[2];     /* part[0]: the pass; cascade: [0] prefix, [1] suffix */
+  int64_t order_off;         /* POD: int ws offset of the launch order (int32)   */
+  int32_t num_blocks;        /* POD: workgroups of the mixed launch              */
+  int32_t batch2;            /* POD: decode requests (batch = prefill requests)  */
+  pkv_plan_part part[2];     /* part[0]: the pass; cascade: [0] prefix, [1] suffix;
+                                POD: [0] prefill, [1] decode */
 } pkv_plan_info;
 
 /* Thread-local message of the last failure on this thread ("" if none). */
@@ -389,6 +399,54 @@ pkv_status pkv_block_sparse_run(const pkv_plan_info* plan, const void* q, const 
                                 const void* v, const int32_t* bsr_indptr_d,
                                 const int32_t* bsr_indices_d, float sm_scale, void* o, float* lse,
                                 void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Mixed prefill + decode batch in one launch (POD attention: named in the
+ * page "FlashInfer: A Kernel Library That Puts Attention, GEMM, and MoE Behind
+ * One API", section "The Feature List: What Is Actually Covered", as the
+ * kernel that fuses prefill and decode for mixed batching; docs index
+ * "flashinfer.pod" > "PODWithPagedKVCacheWrapper").
+ *
+ * The results are exactly those of pkv_prefill_run over the prefill requests
+ * (causal as given) and pkv_decode_run over the decode requests; both read the
+ * same page pools `kv` through their own page tables. plan builds the two
+ * parts with the work-chunk rule (part[0] prefill, part[1] decode; sched as in
+ * the single-kind plans, each part resolving a NULL sched for its own kind)
+ * and an interleaved launch order of their items: an item costs its KV token
+ * count + 1, and the next workgroup takes an item from the part whose emitted
+ * share of its own total cost is smaller (prefill on ties), so every stretch
+ * of the grid mixes MFMA-bound prefill items with HBM-bound decode items. run
+ * launches one kernel for all items, then the merges of each part's split
+ * groups. Either part may be empty (batch_p = 0 or batch_d = 0).
+ * Outputs: o_p [total_qo, Hq, 128] and o_d [batch_d, Hq, 128] in the cache
+ * dtype, lse_p / lse_d float32 or NULL. Needs G <= 16. Errors as
+ * pkv_prefill_plan / pkv_decode_plan. On WORKSPACE_TOO_SMALL, a host_ws of at
+ * least int_ws_required bytes still receives the plan's integer tables (also
+ * true of the other plan calls).
+ * ------------------------------------------------------------------------- */
+pkv_status pkv_pod_plan(const int32_t* qo_indptr_h, const int32_t* kv_indptr_p_h,
+                        const int32_t* last_page_len_p_h, int32_t batch_p, int32_t causal,
+                        const int32_t* kv_indptr_d_h, const int32_t* last_page_len_d_h,
+                        int32_t batch_d, int32_t num_qo_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t page_size, pkv_dtype dtype,
+                        const pkv_sched* sched, void* int_ws, size_t int_ws_bytes,
+                        void* float_ws, size_t float_ws_bytes, void* host_ws,
+                        size_t host_ws_bytes, void* stream, pkv_plan_info* out);
+
+pkv_status pkv_pod_run(const pkv_plan_info* plan, const pkv_paged_kv* kv, const void* q_p,
+                       const int32_t* qo_indptr_d, const int32_t* kv_indptr_p_d,
+                       const int32_t* kv_indices_p_d, void* o_p, float* lse_p, const void* q_d,
+                       const int32_t* kv_indptr_d_d, const int32_t* kv_indices_d_d, void* o_d,
+                       float* lse_d, float sm_scale, void* stream);
+
+/* As pkv_pod_run, recording `attention_done` after the mixed kernel (before
+ * the merges; see pkv_decode_run_timed). */
+pkv_status pkv_pod_run_timed(const pkv_plan_info* plan, const pkv_paged_kv* kv, const void* q_p,
+                             const int32_t* qo_indptr_d, const int32_t* kv_indptr_p_d,
+                             const int32_t* kv_indices_p_d, void* o_p, float* lse_p,
+                             const void* q_d, const int32_t* kv_indptr_d_d,
+                             const int32_t* kv_indices_d_d, void* o_d, float* lse_d,
+                             float sm_scale, void* stream, void* attention_done);
 
 /* ---------------------------------------------------------------------------
  * Appending new K/V rows into a paged cache (docs index "flashinfer.page" >

@@ -100,3 +100,31 @@ def plan_spec(qo_lens, kv_lens, page_size: int, num_kv_heads: int, group_size: i
     spec.items = [r[5] for r in raw]
     spec.num_slots = slot
     return spec
+
+
+def pod_order(items_a, items_b) -> list:
+    """Launch order of a grid that runs two plans' items (the mixed prefill + decode
+    launch): entry i >= 0 is items_a[i], entry -j-1 is items_b[j].
+
+    Rule (this library's; the pages only name the fused prefill + decode kernel):
+    each list keeps its own order; an item costs kv_end - kv_begin + 1; the next
+    entry is taken from the list whose emitted cost, as a fraction of that list's
+    total, is smaller, and from ``items_a`` on ties.
+    """
+    from fractions import Fraction
+    cost_a = [int(it[6]) - int(it[5]) + 1 for it in items_a]
+    cost_b = [int(it[6]) - int(it[5]) + 1 for it in items_b]
+    tot_a, tot_b = sum(cost_a), sum(cost_b)
+    i = j = 0
+    frac_a = frac_b = Fraction(0)
+    order = []
+    while i < len(items_a) or j < len(items_b):
+        if j == len(items_b) or (i < len(items_a) and frac_a <= frac_b):
+            frac_a += Fraction(cost_a[i], tot_a)
+            order.append(i)
+            i += 1
+        else:
+            frac_b += Fraction(cost_b[j], tot_b)
+            order.append(-j - 1)
+            j += 1
+    return order

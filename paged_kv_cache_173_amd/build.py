@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libpkv.so")
-SOURCES = ["api.cpp", "planner.cpp", "decode.hip", "merge.hip", "prefill.hip", "append.hip"]
+SOURCES = ["api.cpp", "planner.cpp", "decode.hip", "merge.hip", "prefill.hip", "append.hip", "pod.hip"]
 ARCH = "gfx950"
 
 

@@ -306,14 +306,11 @@ const int32_t* i_at(const void* base, int64_t off) {
   return reinterpret_cast<const int32_t*>(ws_at(base, off));
 }
 
-// Launches one decode pass (items + merge) writing final rows to o / lse.
-pkv_status run_decode_part(const pkv_plan_info* plan, const pkv_plan_part& part, const void* q,
-                           const pkv_paged_kv* kv, const int32_t* kv_indptr_d,
-                           const int32_t* kv_indices_d, float sm_scale, void* o, float* lse,
-                           pkv::OutKind out_kind, hipStream_t stream,
-                           hipEvent_t attention_done = nullptr,
-                           const pkv::VariantArgs& var = kNoVariant) {
-  const int32_t G = plan->num_qo_heads / plan->num_kv_heads;
+// The decode kernel's arguments for one planned part.
+pkv::DecodeArgs decode_args(const pkv_plan_info* plan, const pkv_plan_part& part, const void* q,
+                            const pkv_paged_kv* kv, const int32_t* kv_indptr_d,
+                            const int32_t* kv_indices_d, float sm_scale, void* o, float* lse,
+                            const pkv::VariantArgs& var) {
   pkv::DecodeArgs a{};
   a.q = q;
   a.k = kv->k;
@@ -326,7 +323,7 @@ pkv_status run_decode_part(const pkv_plan_info* plan, const pkv_plan_part& part,
   a.items = i_at(plan->int_ws, part.items_off);
   a.page_size = plan->page_size;
   a.num_qo_heads = plan->num_qo_heads;
-  a.group = G;
+  a.group = plan->num_qo_heads / plan->num_kv_heads;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.o = o;
   a.lse = lse;
@@ -334,37 +331,15 @@ pkv_status run_decode_part(const pkv_plan_info* plan, const pkv_plan_part& part,
   a.part_lse = f_at(plan->float_ws, part.part_lse_off);
   a.kv_lens = i_at(plan->int_ws, part.kv_len_off);
   a.var = var;
-  hipError_t e = pkv::launch_decode(a, plan->dtype, out_kind, page_mode(plan->page_size),
-                                    part.num_items, stream);
-  if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
-  if (attention_done != nullptr && (e = hipEventRecord(attention_done, stream)) != hipSuccess)
-    return hip_fail(e, "hipEventRecord");
-  if (part.num_groups > 0) {
-    pkv::MergeGroupsArgs m{};
-    m.groups = i_at(plan->int_ws, part.groups_off);
-    m.rows_per_tile = part.rows_per_tile;
-    m.num_qo_heads = plan->num_qo_heads;
-    m.group = G;
-    m.prefill = 0;
-    m.part_o = a.part_o;
-    m.part_lse = a.part_lse;
-    m.o = o;
-    m.lse = lse;
-    m.sinks = var.sinks;
-    e = pkv::launch_merge_groups(m, plan->dtype, out_kind, part.num_groups, stream);
-    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
-  }
-  return PKV_OK;
+  return a;
 }
 
-pkv_status run_prefill_part(const pkv_plan_info* plan, const pkv_plan_part& part, const void* q,
-                            const pkv_paged_kv* kv, const int32_t* qo_indptr_d,
-                            const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
-                            float sm_scale, void* o, float* lse, int32_t num_qo_heads,
-                            pkv::OutKind out_kind, hipStream_t stream,
-                            hipEvent_t attention_done = nullptr,
-                            const pkv::VariantArgs& var = kNoVariant) {
-  const int32_t G = num_qo_heads / plan->num_kv_heads;
+// The prefill kernel's arguments for one planned part.
+pkv::PrefillArgs prefill_args(const pkv_plan_info* plan, const pkv_plan_part& part, const void* q,
+                              const pkv_paged_kv* kv, const int32_t* qo_indptr_d,
+                              const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
+                              float sm_scale, void* o, float* lse, int32_t num_qo_heads,
+                              const pkv::VariantArgs& var) {
   pkv::PrefillArgs a{};
   a.q = q;
   a.k = kv->k;
@@ -379,7 +354,7 @@ pkv_status run_prefill_part(const pkv_plan_info* plan, const pkv_plan_part& part
   a.kv_lens = i_at(plan->int_ws, part.kv_len_off);
   a.page_size = plan->page_size;
   a.num_qo_heads = num_qo_heads;
-  a.group = G;
+  a.group = num_qo_heads / plan->num_kv_heads;
   a.causal = part.causal;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.o = o;
@@ -387,28 +362,66 @@ pkv_status run_prefill_part(const pkv_plan_info* plan, const pkv_plan_part& part
   a.part_o = f_at(plan->float_ws, part.part_o_off);
   a.part_lse = f_at(plan->float_ws, part.part_lse_off);
   a.var = var;
+  return a;
+}
+
+// Merges a part's split groups (if any) into its final rows.
+pkv_status merge_part(const pkv_plan_part& part, bool prefill, const int32_t* qo_indptr_d,
+                      int32_t num_qo_heads, int32_t group, const void* int_ws, void* float_ws,
+                      void* o, float* lse, const float* sinks, pkv_dtype dtype,
+                      pkv::OutKind out_kind, hipStream_t stream) {
+  if (part.num_groups == 0) return PKV_OK;
+  pkv::MergeGroupsArgs m{};
+  m.groups = i_at(int_ws, part.groups_off);
+  m.rows_per_tile = part.rows_per_tile;
+  m.num_qo_heads = num_qo_heads;
+  m.group = group;
+  m.prefill = prefill ? 1 : 0;
+  m.qo_indptr = qo_indptr_d;
+  m.part_o = f_at(float_ws, part.part_o_off);
+  m.part_lse = f_at(float_ws, part.part_lse_off);
+  m.o = o;
+  m.lse = lse;
+  m.sinks = sinks;
+  const hipError_t e = pkv::launch_merge_groups(m, dtype, out_kind, part.num_groups, stream);
+  if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  return PKV_OK;
+}
+
+// Launches one decode pass (items + merge) writing final rows to o / lse.
+pkv_status run_decode_part(const pkv_plan_info* plan, const pkv_plan_part& part, const void* q,
+                           const pkv_paged_kv* kv, const int32_t* kv_indptr_d,
+                           const int32_t* kv_indices_d, float sm_scale, void* o, float* lse,
+                           pkv::OutKind out_kind, hipStream_t stream,
+                           hipEvent_t attention_done = nullptr,
+                           const pkv::VariantArgs& var = kNoVariant) {
+  const pkv::DecodeArgs a =
+      decode_args(plan, part, q, kv, kv_indptr_d, kv_indices_d, sm_scale, o, lse, var);
+  hipError_t e = pkv::launch_decode(a, plan->dtype, out_kind, page_mode(plan->page_size),
+                                    part.num_items, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+  if (attention_done != nullptr && (e = hipEventRecord(attention_done, stream)) != hipSuccess)
+    return hip_fail(e, "hipEventRecord");
+  return merge_part(part, false, nullptr, plan->num_qo_heads, a.group, plan->int_ws,
+                    plan->float_ws, o, lse, var.sinks, plan->dtype, out_kind, stream);
+}
+
+pkv_status run_prefill_part(const pkv_plan_info* plan, const pkv_plan_part& part, const void* q,
+                            const pkv_paged_kv* kv, const int32_t* qo_indptr_d,
+                            const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
+                            float sm_scale, void* o, float* lse, int32_t num_qo_heads,
+                            pkv::OutKind out_kind, hipStream_t stream,
+                            hipEvent_t attention_done = nullptr,
+                            const pkv::VariantArgs& var = kNoVariant) {
+  const pkv::PrefillArgs a = prefill_args(plan, part, q, kv, qo_indptr_d, kv_indptr_d,
+                                          kv_indices_d, sm_scale, o, lse, num_qo_heads, var);
   hipError_t e = pkv::launch_prefill(a, plan->dtype, out_kind, page_mode(plan->page_size),
                                      part.num_items, stream);
   if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
   if (attention_done != nullptr && (e = hipEventRecord(attention_done, stream)) != hipSuccess)
     return hip_fail(e, "hipEventRecord");
-  if (part.num_groups > 0) {
-    pkv::MergeGroupsArgs m{};
-    m.groups = i_at(plan->int_ws, part.groups_off);
-    m.rows_per_tile = part.rows_per_tile;
-    m.num_qo_heads = num_qo_heads;
-    m.group = G;
-    m.prefill = 1;
-    m.qo_indptr = qo_indptr_d;
-    m.part_o = a.part_o;
-    m.part_lse = a.part_lse;
-    m.o = o;
-    m.lse = lse;
-    m.sinks = var.sinks;
-    e = pkv::launch_merge_groups(m, plan->dtype, out_kind, part.num_groups, stream);
-    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
-  }
-  return PKV_OK;
+  return merge_part(part, true, qo_indptr_d, num_qo_heads, a.group, plan->int_ws, plan->float_ws,
+                    o, lse, var.sinks, plan->dtype, out_kind, stream);
 }
 
 }  // namespace
@@ -867,6 +880,116 @@ pkv_status pkv_cascade_run(const pkv_plan_info* plan, const void* q, const pkv_p
   hipError_t e = pkv::launch_merge2_f32_to(a_o, a_lse, b_o, b_lse, o, lse, rows,
                                            static_cast<int32_t>(D), plan->dtype, hs);
   if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  return ok();
+}
+
+pkv_status pkv_pod_plan(const int32_t* qo_indptr_h, const int32_t* kv_indptr_p_h,
+                        const int32_t* last_page_len_p_h, int32_t batch_p, int32_t causal,
+                        const int32_t* kv_indptr_d_h, const int32_t* last_page_len_d_h,
+                        int32_t batch_d, int32_t num_qo_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t page_size, pkv_dtype dtype,
+                        const pkv_sched* sched, void* int_ws, size_t int_ws_bytes,
+                        void* float_ws, size_t float_ws_bytes, void* host_ws,
+                        size_t host_ws_bytes, void* stream, pkv_plan_info* out) {
+  if (out == nullptr) return fail(PKV_ERR_INVALID_ARG, "out is NULL");
+  pkv_status st;
+  if ((st = check_heads(num_qo_heads, num_kv_heads))) return st;
+  if ((st = check_head_dim_dtype(head_dim, dtype))) return st;
+  if (causal != 0 && causal != 1) return fail(PKV_ERR_INVALID_ARG, "causal must be 0 or 1");
+  const int32_t G = num_qo_heads / num_kv_heads;
+  if (G > kMaxDecodeGroup)
+    return fail(PKV_ERR_UNSUPPORTED, "the mixed launch supports num_qo_heads / num_kv_heads <= 16");
+  std::vector<int64_t> kv_p, qo_p, kv_d;
+  if ((st = check_page_table(kv_indptr_p_h, last_page_len_p_h, batch_p, page_size, &kv_p)))
+    return st;
+  if ((st = check_qo_indptr(qo_indptr_h, batch_p, &qo_p))) return st;
+  if ((st = check_page_table(kv_indptr_d_h, last_page_len_d_h, batch_d, page_size, &kv_d)))
+    return st;
+  int64_t total_qo = 0;
+  for (int64_t qn : qo_p) total_qo += qn;
+  if (total_qo * num_qo_heads > INT32_MAX)
+    return fail(PKV_ERR_INVALID_ARG, "total query rows overflow int32");
+  pkv_sched sp, sd;
+  if ((st = resolve_sched(sched, PKV_KIND_PREFILL, &sp))) return st;
+  if ((st = resolve_sched(sched, PKV_KIND_DECODE, &sd))) return st;
+  std::vector<int64_t> qo_d(batch_d, 1);
+  pkv::HostPlan hp, hd;
+  std::string err;
+  if (!pkv::build_plan(make_input(qo_p, kv_p, page_size, num_kv_heads, G, kRowsPerPrefillTile,
+                                  causal != 0, sp),
+                       &hp, &err) ||
+      !pkv::build_plan(make_input(qo_d, kv_d, page_size, num_kv_heads, G, G, false, sd), &hd,
+                       &err))
+    return fail(PKV_ERR_INVALID_ARG, err);
+  const std::vector<int32_t> order = pkv::interleave_items(hp.items, hd.items);
+  fill_header(out, PKV_KIND_POD, dtype, batch_p, num_qo_heads, num_kv_heads, head_dim, page_size,
+              static_cast<int32_t>(total_qo), sp);
+  out->batch2 = batch_d;
+  out->num_blocks = static_cast<int32_t>(order.size());
+  Layout lay;
+  place_part(hp, batch_p, kRowsPerPrefillTile, causal, &lay, &out->part[0]);
+  place_part(hd, batch_d, G, 0, &lay, &out->part[1]);
+  out->order_off = lay.int_bytes;
+  lay.int_bytes = align_up(lay.int_bytes + static_cast<int64_t>(order.size()) * 4);
+  if (host_ws != nullptr && host_ws_bytes >= static_cast<size_t>(lay.int_bytes)) {
+    char* h = static_cast<char*>(host_ws);
+    write_part(hp, kv_p, out->part[0], h);
+    write_part(hd, kv_d, out->part[1], h);
+    if (!order.empty()) std::memcpy(h + out->order_off, order.data(), order.size() * 4);
+  }
+  if ((st = commit_plan(lay, int_ws, int_ws_bytes, float_ws, float_ws_bytes, host_ws,
+                        host_ws_bytes, static_cast<hipStream_t>(stream), out)))
+    return st;
+  return ok();
+}
+
+pkv_status pkv_pod_run(const pkv_plan_info* plan, const pkv_paged_kv* kv, const void* q_p,
+                       const int32_t* qo_indptr_d, const int32_t* kv_indptr_p_d,
+                       const int32_t* kv_indices_p_d, void* o_p, float* lse_p, const void* q_d,
+                       const int32_t* kv_indptr_d_d, const int32_t* kv_indices_d_d, void* o_d,
+                       float* lse_d, float sm_scale, void* stream) {
+  return pkv_pod_run_timed(plan, kv, q_p, qo_indptr_d, kv_indptr_p_d, kv_indices_p_d, o_p, lse_p,
+                           q_d, kv_indptr_d_d, kv_indices_d_d, o_d, lse_d, sm_scale, stream,
+                           nullptr);
+}
+
+pkv_status pkv_pod_run_timed(const pkv_plan_info* plan, const pkv_paged_kv* kv, const void* q_p,
+                             const int32_t* qo_indptr_d, const int32_t* kv_indptr_p_d,
+                             const int32_t* kv_indices_p_d, void* o_p, float* lse_p,
+                             const void* q_d, const int32_t* kv_indptr_d_d,
+                             const int32_t* kv_indices_d_d, void* o_d, float* lse_d,
+                             float sm_scale, void* stream, void* attention_done) {
+  pkv_status st;
+  if ((st = check_scale(sm_scale))) return st;
+  if ((st = check_plan(plan, PKV_KIND_POD))) return st;
+  if ((st = check_kv(kv, plan))) return st;
+  if (plan->total_qo > 0 && (q_p == nullptr || o_p == nullptr || qo_indptr_d == nullptr ||
+                             kv_indptr_p_d == nullptr || kv_indices_p_d == nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "q_p, o_p, qo_indptr, kv_indptr_p or kv_indices_p is NULL");
+  if (plan->batch2 > 0 && (q_d == nullptr || o_d == nullptr || kv_indptr_d_d == nullptr ||
+                           kv_indices_d_d == nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "q_d, o_d, kv_indptr_d or kv_indices_d is NULL");
+  if (!aligned16(q_p) || !aligned16(o_p) || !aligned16(q_d) || !aligned16(o_d))
+    return fail(PKV_ERR_INVALID_ARG, "q / o must be 16-byte aligned");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  pkv::PodArgs a{};
+  a.p = prefill_args(plan, plan->part[0], q_p, kv, qo_indptr_d, kv_indptr_p_d, kv_indices_p_d,
+                     sm_scale, o_p, lse_p, plan->num_qo_heads, kNoVariant);
+  a.d = decode_args(plan, plan->part[1], q_d, kv, kv_indptr_d_d, kv_indices_d_d, sm_scale, o_d,
+                    lse_d, kNoVariant);
+  a.order = i_at(plan->int_ws, plan->order_off);
+  hipError_t e = pkv::launch_pod(a, plan->dtype, page_mode(plan->page_size), plan->num_blocks, s);
+  if (e != hipSuccess) return hip_fail(e, "mixed prefill + decode kernel launch");
+  if (attention_done != nullptr &&
+      (e = hipEventRecord(static_cast<hipEvent_t>(attention_done), s)) != hipSuccess)
+    return hip_fail(e, "hipEventRecord");
+  if ((st = merge_part(plan->part[0], true, qo_indptr_d, plan->num_qo_heads, a.p.group,
+                       plan->int_ws, plan->float_ws, o_p, lse_p, nullptr, plan->dtype,
+                       pkv::kOutStorage, s)))
+    return st;
+  if ((st = merge_part(plan->part[1], false, nullptr, plan->num_qo_heads, a.d.group, plan->int_ws,
+                       plan->float_ws, o_d, lse_d, nullptr, plan->dtype, pkv::kOutStorage, s)))
+    return st;
   return ok();
 }
 

@@ -101,6 +101,16 @@ struct AppendArgs {
   int64_t nnz;
 };
 
+// One launch of prefill and decode items (the mixed-batch kernel): entry i of
+// `order` names the item workgroup i runs (>= 0: prefill item; < 0: decode
+// item -e-1). The two halves keep their own argument blocks; both read the
+// same page pools.
+struct PodArgs {
+  PrefillArgs p;
+  DecodeArgs d;
+  const int32_t* order;       // device [num_prefill_items + num_decode_items]
+};
+
 struct MergeGroupsArgs {
   const int32_t* groups;      // device [num_groups][8], or NULL: implicit (single decode)
   int32_t implicit_nchunks;
@@ -130,6 +140,10 @@ hipError_t launch_merge_groups(const MergeGroupsArgs& a, int32_t storage_dtype, 
                                int32_t num_groups, hipStream_t stream);
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+
+// Mixed prefill + decode launch; outputs are in the storage dtype.
+hipError_t launch_pod(const PodArgs& a, int32_t storage_dtype, PageMode mode, int32_t grid,
+                      hipStream_t stream);
 
 // Public merges: v dtype in {F16, BF16, F32}; rows = n * H.
 hipError_t launch_merge2(const void* va, const float* sa, const void* vb, const float* sb,

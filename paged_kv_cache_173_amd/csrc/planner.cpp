@@ -118,4 +118,29 @@ bool build_plan(const PlanInput& in, HostPlan* out, std::string* err) {
   return true;
 }
 
+std::vector<int32_t> interleave_items(const std::vector<PlanItem>& a,
+                                      const std::vector<PlanItem>& b) {
+  auto cost = [](const PlanItem& it) -> int64_t { return int64_t{it.kv_end} - it.kv_begin + 1; };
+  int64_t total_a = 0, total_b = 0;
+  for (const PlanItem& it : a) total_a += cost(it);
+  for (const PlanItem& it : b) total_b += cost(it);
+  std::vector<int32_t> order;
+  order.reserve(a.size() + b.size());
+  size_t i = 0, j = 0;
+  int64_t done_a = 0, done_b = 0;
+  while (i < a.size() || j < b.size()) {
+    // done_a / total_a <= done_b / total_b, in integers (both totals > 0 when
+    // their list is non-empty; products stay far below 2^63)
+    const bool take_a = j == b.size() || (i < a.size() && done_a * total_b <= done_b * total_a);
+    if (take_a) {
+      done_a += cost(a[i]);
+      order.push_back(static_cast<int32_t>(i++));
+    } else {
+      done_b += cost(b[j]);
+      order.push_back(-static_cast<int32_t>(j++) - 1);
+    }
+  }
+  return order;
+}
+
 }  // namespace pkv

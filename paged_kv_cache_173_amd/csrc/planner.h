@@ -53,4 +53,13 @@ struct HostPlan {
 // Applies the rule. Returns false (with *err set) if a count overflows int32.
 bool build_plan(const PlanInput& in, HostPlan* out, std::string* err);
 
+// Launch order of one grid that runs the items of two plans (the mixed
+// prefill + decode launch): entry >= 0 is item `entry` of `a`, entry < 0 is
+// item -entry-1 of `b`. Each list keeps its own order. An item costs its KV
+// token count plus one; the next entry comes from the list whose emitted share
+// of its own total cost is smaller (a on ties), so the two kinds advance at the
+// same relative pace and every stretch of the grid mixes them.
+std::vector<int32_t> interleave_items(const std::vector<PlanItem>& a,
+                                      const std::vector<PlanItem>& b);
+
 }  // namespace pkv

@@ -34,7 +34,7 @@ PKV_ERR_HIP = 5
 # dtypes
 PKV_F16, PKV_BF16, PKV_F32 = 0, 1, 2
 # plan kinds
-PKV_KIND_DECODE, PKV_KIND_PREFILL, PKV_KIND_CASCADE, PKV_KIND_BLOCK_SPARSE = 1, 2, 3, 4
+PKV_KIND_DECODE, PKV_KIND_PREFILL, PKV_KIND_CASCADE, PKV_KIND_BLOCK_SPARSE, PKV_KIND_POD = 1, 2, 3, 4, 5
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -71,7 +71,8 @@ class pkv_plan_info(ctypes.Structure):
                 ("head_dim", _I32), ("page_size", _I32), ("total_qo", _I32),
                 ("sched", pkv_sched), ("int_ws", _P), ("float_ws", _P),
                 ("int_ws_required", _I64), ("float_ws_required", _I64),
-                ("cascade_state_off", _I64), ("part", pkv_plan_part * 2)]
+                ("cascade_state_off", _I64), ("order_off", _I64), ("num_blocks", _I32),
+                ("batch2", _I32), ("part", pkv_plan_part * 2)]
 
 
 def _sig(name, restype, argtypes):
@@ -138,6 +139,17 @@ _lib_cascade_plan = _sig("pkv_cascade_plan", _I32,
 _lib_cascade_run = _sig("pkv_cascade_run", _I32,
                         [ctypes.POINTER(pkv_plan_info), _P, ctypes.POINTER(pkv_paged_kv), _P, _P,
                          _P, _F32, _P, _P, _P])
+
+_lib_pod_plan = _sig("pkv_pod_plan", _I32,
+                     [_I32P, _I32P, _I32P, _I32, _I32, _I32P, _I32P, _I32, _I32, _I32, _I32, _I32,
+                      _I32, ctypes.POINTER(pkv_sched), _P, _SZ, _P, _SZ, _P, _SZ, _P,
+                      ctypes.POINTER(pkv_plan_info)])
+_lib_pod_run_timed = _sig("pkv_pod_run_timed", _I32,
+                          [ctypes.POINTER(pkv_plan_info), ctypes.POINTER(pkv_paged_kv), _P, _P,
+                           _P, _P, _P, _P, _P, _P, _P, _P, _P, _F32, _P, _P])
+_lib_pod_run = _sig("pkv_pod_run", _I32,
+                    [ctypes.POINTER(pkv_plan_info), ctypes.POINTER(pkv_paged_kv), _P, _P, _P, _P,
+                     _P, _P, _P, _P, _P, _P, _P, _F32, _P])
 
 if _lib_plan_info_size() != ctypes.sizeof(pkv_plan_info):
     raise ImportError("pkv_plan_info layout of the binding differs from the library's")
@@ -494,6 +506,52 @@ def pkv_cascade_run(plan: pkv_plan_info, q, k_cache, v_cache, prefix_indices_d, 
                             suffix_indices_d.data_ptr(), float(sm_scale), o.data_ptr(), _ptr(lse),
                             _stream(stream)), "pkv_cascade_run")
     return o, lse
+
+
+def pkv_pod_plan(qo_indptr, kv_indptr_p, last_page_len_p, causal, kv_indptr_d, last_page_len_d,
+                 num_qo_heads, num_kv_heads, head_dim, page_size, dtype, workspace: Workspace,
+                 sched=None, stream=None) -> pkv_plan_info:
+    """Plan a mixed batch: prefill requests (qo_indptr, kv_indptr_p, last_page_len_p) and
+    decode requests (kv_indptr_d, last_page_len_d), host arrays, one launch."""
+    qop, kvp, lpp = _host_i32(qo_indptr), _host_i32(kv_indptr_p), _host_i32(last_page_len_p)
+    kvd, lpd = _host_i32(kv_indptr_d), _host_i32(last_page_len_d)
+    code = dtype if isinstance(dtype, int) else dtype_code(dtype)
+
+    def call(ws, info):
+        return _lib_pod_plan(_i32p(qop), _i32p(kvp), _i32p(lpp), len(kvp) - 1, int(causal),
+                             _i32p(kvd), _i32p(lpd), len(kvd) - 1, num_qo_heads, num_kv_heads,
+                             head_dim, page_size, code, _sched_arg(sched), *ws.args(),
+                             _stream(stream), ctypes.byref(info))
+    return _plan_with_growth(call, workspace, "pkv_pod_plan")
+
+
+def pkv_pod_host_order(plan: pkv_plan_info, host_ws) -> np.ndarray:
+    """The launch order a plan wrote into its host workspace (int32 [num_blocks])."""
+    raw = np.frombuffer(host_ws, dtype=np.uint8)
+    return raw[plan.order_off:plan.order_off + 4 * plan.num_blocks].view(np.int32).copy()
+
+
+def pkv_pod_run(plan: pkv_plan_info, k_cache, v_cache, q_p, qo_indptr_d, kv_indptr_p_d,
+                kv_indices_p_d, q_d, kv_indptr_d_d, kv_indices_d_d, sm_scale: float, o_p=None,
+                lse_p=None, o_d=None, lse_d=None, stream=None, attention_done=None):
+    """One launch for both parts -> (o_p, lse_p, o_d, lse_d); records the torch.cuda.Event
+    `attention_done` (if given) after the mixed kernel, before the merges."""
+    kv = paged_kv(k_cache, v_cache)
+    q_p, q_d = q_p.contiguous(), q_d.contiguous()
+    o_p = torch.empty_like(q_p) if o_p is None else o_p
+    o_d = torch.empty_like(q_d) if o_d is None else o_d
+    f32 = dict(dtype=torch.float32, device=q_p.device)
+    lse_p = torch.empty(q_p.shape[:2], **f32) if lse_p is None else lse_p
+    lse_d = torch.empty(q_d.shape[:2], **f32) if lse_d is None else lse_d
+    args = (ctypes.byref(plan), ctypes.byref(kv), q_p.data_ptr(), qo_indptr_d.data_ptr(),
+            kv_indptr_p_d.data_ptr(), kv_indices_p_d.data_ptr(), o_p.data_ptr(), _ptr(lse_p),
+            q_d.data_ptr(), kv_indptr_d_d.data_ptr(), kv_indices_d_d.data_ptr(), o_d.data_ptr(),
+            _ptr(lse_d), float(sm_scale), _stream(stream))
+    if attention_done is None:
+        _check(_lib_pod_run(*args), "pkv_pod_run")
+    else:
+        _check(_lib_pod_run_timed(*args, _event(attention_done)), "pkv_pod_run_timed")
+    return o_p, lse_p, o_d, lse_d
 
 
 def pkv_block_sparse_plan(bsr_indptr, bsr_indices, num_qo_tokens, num_kv_tokens, row_block,

@@ -364,3 +364,59 @@ def block_sparse(seed=173006, num_qo_tokens=8192, num_kv_tokens=8192, row_block=
     return BlockSparseWorkload(dtype, num_qo_heads, num_kv_heads, head_dim,
                                1.0 / math.sqrt(head_dim), q, k, v, indptr, indices, row_block,
                                col_block, meta={"seed": seed, "density": density})
+
+
+@dataclass
+class PodWorkload:
+    """A mixed batch: prefill requests and decode requests whose page tables point
+    into one shared page pool (``prefill.kv`` and ``decode.kv`` hold the same pool
+    arrays)."""
+    kind = "pod"                 # (class attribute, not a field)
+    prefill: Workload
+    decode: Workload
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def dtype(self) -> str:
+        return self.prefill.dtype
+
+
+def pod(seed=173007, p_batch=16, qo_min=128, qo_max=1024, prefix_min=0, prefix_max=2048,
+        d_batch=64, kv_min=512, kv_max=4096, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+        page_size=16, dtype="bf16", causal=True, canary=False, qo_lens=None, prefix_lens=None,
+        d_lens=None):
+    """The causal prefill workload's requests and the batch decode workload's requests
+    in one batch over one pool. Draw order: prefill query lengths, prefixes, decode
+    lengths, the pool (prefill requests' pages first), prefill q, K pool, V pool,
+    decode q."""
+    rng = np.random.default_rng(seed)
+    if qo_lens is None:
+        qo_lens = rng.integers(qo_min, qo_max + 1, size=p_batch)
+    if prefix_lens is None:
+        prefix_lens = rng.integers(prefix_min, prefix_max + 1, size=len(qo_lens))
+    if d_lens is None:
+        d_lens = rng.integers(kv_min, kv_max + 1, size=d_batch)
+    qo_lens = np.asarray(qo_lens, dtype=np.int64)
+    prefix_lens = np.asarray(prefix_lens, dtype=np.int64)
+    d_lens = np.asarray(d_lens, dtype=np.int64)
+    p_lens = qo_lens + prefix_lens
+    Bp = len(qo_lens)
+    kv, q_p, _ = make_paged(rng, np.concatenate([p_lens, d_lens]), page_size, num_kv_heads,
+                            head_dim, dtype, (int(qo_lens.sum()), num_qo_heads, head_dim))
+    q_d = normal_bits(rng, (len(d_lens), num_qo_heads, head_dim), dtype)
+    if canary:
+        canary_tails(kv, dtype)
+    cut = int(kv.kv_indptr[Bp])
+    kv_p = PagedKV(kv.k_cache, kv.v_cache, kv.kv_indptr[:Bp + 1].copy(), kv.kv_indices[:cut].copy(),
+                   kv.last_page_len[:Bp].copy(), page_size)
+    kv_d = PagedKV(kv.k_cache, kv.v_cache, (kv.kv_indptr[Bp:] - cut).astype(np.int32),
+                   kv.kv_indices[cut:].copy(), kv.last_page_len[Bp:].copy(), page_size)
+    qo_indptr = np.zeros(Bp + 1, dtype=np.int32)
+    qo_indptr[1:] = np.cumsum(qo_lens)
+    scale = 1.0 / math.sqrt(head_dim)
+    wp = Workload("prefill", dtype, num_qo_heads, num_kv_heads, head_dim, scale, q_p, kv=kv_p,
+                  qo_indptr=qo_indptr, causal=causal,
+                  meta={"seed": seed, "qo_lens": qo_lens, "kv_lens": p_lens})
+    wd = Workload("decode", dtype, num_qo_heads, num_kv_heads, head_dim, scale, q_d, kv=kv_d,
+                  meta={"seed": seed, "kv_lens": d_lens})
+    return PodWorkload(wp, wd, meta={"seed": seed})
