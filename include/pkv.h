@@ -194,10 +194,11 @@ size_t pkv_plan_info_size(void);
  * wg_per_cu = 4, min_chunk_tokens = 256. Needs a GPU. */
 pkv_status pkv_default_sched(int32_t device, pkv_sched* out);
 
-/* Defaults tuned to one kernel: as pkv_default_sched, but wg_per_cu is the
- * number of workgroups of that kind's kernel resident on one CU (decode:
- * the decode kernel; prefill: the prefill kernel), so one wave of workgroups
- * covers the chip. A plan given a NULL sched uses this for its own kind (the
+/* Defaults tuned to one kernel: as pkv_default_sched, but wg_per_cu follows
+ * the number of workgroups of that kind's kernel resident on one CU (occ):
+ * prefill: occ (one wave of items covers the chip); decode: (5*occ+1)/2, about
+ * two and a half waves of items, so that the longest-first order evens out the
+ * last one. A plan given a NULL sched uses this for its own kind (the
  * cascade: prefill for level 0, decode for level 1). Needs a GPU. */
 pkv_status pkv_default_sched_for(pkv_kind kind, int32_t device, pkv_sched* out);
 

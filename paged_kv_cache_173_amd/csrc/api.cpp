@@ -21,6 +21,9 @@ thread_local std::string g_error;
 constexpr uint32_t kPlanMagic = 0x31564b50u;  // "PKV1"
 constexpr int64_t kAlign = 256;
 constexpr int32_t kRowsPerPrefillTile = 128;
+// The mixed prefill + decode kernel runs 128-row prefill items (one row block
+// per wave, two workgroups per CU), whatever the prefill kernel uses.
+constexpr int32_t kRowsPerPodPrefillTile = 128;
 constexpr int32_t kMaxDecodeGroup = 16;
 
 pkv_status fail(pkv_status st, const std::string& msg) {
@@ -356,6 +359,7 @@ pkv::PrefillArgs prefill_args(const pkv_plan_info* plan, const pkv_plan_part& pa
   a.num_qo_heads = num_qo_heads;
   a.group = num_qo_heads / plan->num_kv_heads;
   a.causal = part.causal;
+  a.rows_per_tile = part.rows_per_tile;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.o = o;
   a.lse = lse;
@@ -456,7 +460,11 @@ pkv_status pkv_default_sched_for(pkv_kind kind, int32_t device, pkv_sched* out) 
   if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return hip_fail(e, "hipSetDevice");
   const int32_t occ = kind == PKV_KIND_DECODE ? pkv::decode_occupancy() : pkv::prefill_occupancy();
   if (cur != device) (void)hipSetDevice(cur);
-  if (occ > 0) out->wg_per_cu = occ;
+  // Decode: about two and a half waves of items per resident workgroup, so that
+  // the longest-first order evens out the last wave (one wave left ~5 % idle at
+  // the end on the 64-request and 4 x 128k-token workloads). Prefill: one wave;
+  // its tiles already give several items per workgroup.
+  if (occ > 0) out->wg_per_cu = kind == PKV_KIND_DECODE ? (5 * occ + 1) / 2 : occ;
   return ok();
 }
 
@@ -915,7 +923,7 @@ pkv_status pkv_pod_plan(const int32_t* qo_indptr_h, const int32_t* kv_indptr_p_h
   std::vector<int64_t> qo_d(batch_d, 1);
   pkv::HostPlan hp, hd;
   std::string err;
-  if (!pkv::build_plan(make_input(qo_p, kv_p, page_size, num_kv_heads, G, kRowsPerPrefillTile,
+  if (!pkv::build_plan(make_input(qo_p, kv_p, page_size, num_kv_heads, G, kRowsPerPodPrefillTile,
                                   causal != 0, sp),
                        &hp, &err) ||
       !pkv::build_plan(make_input(qo_d, kv_d, page_size, num_kv_heads, G, G, false, sd), &hd,
@@ -927,7 +935,7 @@ pkv_status pkv_pod_plan(const int32_t* qo_indptr_h, const int32_t* kv_indptr_p_h
   out->batch2 = batch_d;
   out->num_blocks = static_cast<int32_t>(order.size());
   Layout lay;
-  place_part(hp, batch_p, kRowsPerPrefillTile, causal, &lay, &out->part[0]);
+  place_part(hp, batch_p, kRowsPerPodPrefillTile, causal, &lay, &out->part[0]);
   place_part(hd, batch_d, G, 0, &lay, &out->part[1]);
   out->order_off = lay.int_bytes;
   lay.int_bytes = align_up(lay.int_bytes + static_cast<int64_t>(order.size()) * 4);

@@ -75,6 +75,7 @@ struct PrefillArgs {
   int32_t num_qo_heads;
   int32_t group;              // G <= 128
   int32_t causal;
+  int32_t rows_per_tile;      // query rows of an item (128: the plan and the kernel agree)
   float scale_log2;           // sm_scale * log2(e)
   void* o;                    // final output rows [total_qo*Hq][128]
   float* lse;                 // [total_qo*Hq] or NULL

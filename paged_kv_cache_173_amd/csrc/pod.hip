@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256, 2) void pod_kernel(const PodArgs a) {
   using OUT = typename T::elem;
   const int e = a.order[blockIdx.x];
   if (e >= 0) {
-    prefill_item<T, OUT, MODE, false>(a.p, a.p.items + 8 * e);
+    prefill_item<T, OUT, MODE, false, 1>(a.p, a.p.items + 8 * e);
   } else {
     const int32_t* it = a.d.items + 8 * (-e - 1);
     float* m = reinterpret_cast<float*>(sV0);

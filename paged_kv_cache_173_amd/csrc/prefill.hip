@@ -9,15 +9,18 @@ namespace {
 
 template <class T, class OUT, int MODE, bool VAR>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(const PrefillArgs a) {
-  prefill_item<T, OUT, MODE, VAR>(a, a.items + 8 * blockIdx.x);
+  prefill_item<T, OUT, MODE, VAR, 1>(a, a.items + 8 * blockIdx.x);
 }
+
+
 
 template <class T, class OUT, bool VAR>
 void launch_prefill_mode(const PrefillArgs& a, PageMode mode, int32_t grid, hipStream_t s) {
-  if (mode == kPagedUniform)
+  if (mode == kPagedUniform) {
     hipLaunchKernelGGL((prefill_kernel<T, OUT, kPagedUniform, VAR>), dim3(grid), dim3(256), 0, s, a);
-  else
+  } else {
     hipLaunchKernelGGL((prefill_kernel<T, OUT, kPagedGeneric, VAR>), dim3(grid), dim3(256), 0, s, a);
+  }
 }
 
 template <class T, class OUT>
@@ -46,6 +49,7 @@ int32_t prefill_occupancy() {
 hipError_t launch_prefill(const PrefillArgs& a, int32_t storage_dtype, OutKind out,
                           PageMode mode, int32_t grid, hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
+  if (a.rows_per_tile != kTileRows) return hipErrorInvalidValue;
   if (storage_dtype == 0) {
     return out == kOutF32 ? launch_prefill_t<F16, float>(a, mode, grid, stream)
                           : launch_prefill_t<F16, _Float16>(a, mode, grid, stream);

@@ -143,10 +143,18 @@ __shared__ __attribute__((aligned(1024))) char sV1[kTileBytes];
 __shared__ __attribute__((aligned(1024))) char sV2[kTileBytes];
 __shared__ __attribute__((aligned(1024))) char sV3[kTileBytes];
 
-template <class T, class OUT, int MODE, bool VAR>
+// RB = row blocks per wave: wave w owns rows 32*RB*w .. 32*RB*(w+1)-1 of an
+// item of 128*RB rows, in RB blocks of 32. Every K and V operand read from LDS
+// feeds RB MFMAs (one per block). The kernels use RB = 1 (two waves per SIMD,
+// 256 VGPRs). RB = 2 halves the LDS reads per MFMA but needs about 330
+// registers per lane, so one wave per SIMD; with the compiler placing the
+// score accumulators in AGPRs (every softmax touch then copies them out) it
+// gave bit-identical results 23 % slower on the causal prefill workload.
+template <class T, class OUT, int MODE, bool VAR, int RB = 1>
 __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t* it) {
   using elem = typename T::elem;
   constexpr int D = kHeadDim;
+  constexpr int kRows = kTileRows * RB;    // query rows of one item
   auto kbuf = [&](auto ph) -> char* {
     constexpr int i = decltype(ph)::value & 3;
     if constexpr (i == 0) return sK0;
@@ -178,39 +186,52 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
   const int Q = uni(a.qo_indptr[b + 1]) - q0;
   const int L = uni(a.kv_lens[b]);
 
-  // This lane's query row.
-  const int prow = tile * kTileRows + 32 * wave + lr;     // GQA-packed row in the request
-  const bool row_ok = prow < Q * G;
-  const int qtok = prow / G;
-  const int head = g * G + (prow - qtok * G);
-  const int lim = qtok + L - Q;                            // last visible key (causal)
+  // This lane's query rows (one per block).
+  const int row0 = tile * kRows + 32 * RB * wave;          // the wave's first row
+  bool row_ok[RB];
+  int qtok[RB], head[RB], lim[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int prow = row0 + 32 * rb + lr;                  // GQA-packed row in the request
+    row_ok[rb] = prow < Q * G;
+    qtok[rb] = prow / G;
+    head[rb] = g * G + (prow - qtok[rb] * G);
+    lim[rb] = qtok[rb] + L - Q;                            // last visible key (causal)
+  }
   // Smallest causal limit of the wave (its first row): tiles that end at or
   // before it need no causal mask for any row of the wave.
-  const int lim_wave = (tile * kTileRows + 32 * wave) / G + L - Q;
+  const int lim_wave = row0 / G + L - Q;
   // Keys past this one need a mask for some row of the wave (the causal
   // limit of the wave's first row, or the item's end).
   const int mask_from = a.causal ? min(k1 - 1, lim_wave) : k1 - 1;
   // Sliding window (VAR): the row's first visible key, and the largest of
   // them in the wave (its last row's): tiles starting below it need the
   // window mask for some row of the wave.
-  int wlo = 0, win_from = 0;
+  int wlo[RB], win_from = 0;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) wlo[rb] = 0;
   if constexpr (VAR) {
     if (a.var.window_left >= 0) {
-      wlo = lim - a.var.window_left;
-      win_from = (tile * kTileRows + 32 * wave + 31) / G + L - Q - a.var.window_left;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) wlo[rb] = lim[rb] - a.var.window_left;
+      win_from = (row0 + 32 * RB - 1) / G + L - Q - a.var.window_left;
     } else {
-      wlo = win_from = INT32_MIN / 4;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) wlo[rb] = INT32_MIN / 4;
+      win_from = INT32_MIN / 4;
     }
   }
   const bool capped = VAR && a.var.cap_out > 0.f;
 
-  // q^T as the B operand: lane holds q[row lr][d = 16kk + 8*half .. +7].
-  u32x4 qv[8];
-  {
-    const elem* qp = static_cast<const elem*>(a.q) +
-                     (static_cast<int64_t>(q0 + qtok) * a.num_qo_heads + head) * D + 8 * half;
+  // q^T as the B operand: lane holds q[row][d = 16kk + 8*half .. +7] of each block.
+  u32x4 qv[RB][8];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qv[kk] = row_ok ? load_16B(qp + 16 * kk) : u32x4{0, 0, 0, 0};
+  for (int rb = 0; rb < RB; ++rb) {
+    const elem* qp = static_cast<const elem*>(a.q) +
+                     (static_cast<int64_t>(q0 + qtok[rb]) * a.num_qo_heads + head[rb]) * D + 8 * half;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      qv[rb][kk] = row_ok[rb] ? load_16B(qp + 16 * kk) : u32x4{0, 0, 0, 0};
   }
 
   // ---- staging: wave w fetches token rows 8w .. 8w+7 of a tile; load j
@@ -298,8 +319,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
     }
   };
 
-  // Row state. The exponent reference m_ref (log2 domain, scaled) is the row
-  // maximum seen so far up to the lazy slack; weights are
+  // Row state (one per block). The exponent reference m_ref (log2 domain,
+  // scaled) is the row maximum seen so far up to the lazy slack; weights are
   // exp2(scale_log2 * s - m_ref) rounded once to the storage dtype, and the
   // normalisation of O uses the sum of those rounded weights (O is then an
   // exact convex combination of V rows). The LSE needs the sum of the
@@ -307,21 +328,27 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
   // up to 2^-8 relative, ln(1 + 2^-8) = 3.9e-3 in the LSE for a row with few
   // keys, so bf16 keeps a second, fp32 sum; fp16's 2^-11 (4.9e-4) uses the
   // rounded sum for both.
-  float m_ref = neg_inf();
-  float neg_m = 0.f;          // -m_ref, or 0 while m_ref = -inf
-  // Raw-score threshold (m_ref + slack) / scale_log2: a tile needs the
-  // rescale path only if some lane holds a score above it (any rounding in
-  // it only moves the point at which the reference is refreshed).
-  float thr = neg_inf();
+  float m_ref[RB], neg_m[RB], thr[RB], l_run[RB], l_lse[RB];
+  // neg_m: -m_ref, or 0 while m_ref = -inf. thr: the raw-score threshold
+  // (m_ref + slack) / scale_log2: a tile needs the rescale path only if some
+  // lane holds a score above it (any rounding in it only moves the point at
+  // which the reference is refreshed). l_run / l_lse: this lane's share of the
+  // row's rounded / unrounded weight sum.
   const float inv_scale_log2 = 1.f / a.scale_log2;
-  float l_run = 0.f;          // this lane's share of the row's rounded-weight sum
   constexpr bool kExactLse = std::is_same_v<T, BF16>;
-  float l_lse = 0.f;          // ... and of its unrounded-weight sum (kExactLse)
-  f32x16 acc[4];              // acc[mb][i]: row lr, d = 32mb + 8(i/4) + 4*half + i%4
+  f32x16 acc[RB][4];          // acc[rb][mb][i]: row lr of block rb, d = 32mb + 8(i/4) + 4*half + i%4
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int rb = 0; rb < RB; ++rb) {
+    m_ref[rb] = neg_inf();
+    neg_m[rb] = 0.f;
+    thr[rb] = neg_inf();
+    l_run[rb] = 0.f;
+    l_lse[rb] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[rb][mb][i] = 0.f;
+  }
 
   const int ntiles = (k1 - k0 + KT - 1) / KT;
 
@@ -347,39 +374,51 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) va[mb] = v_lane ^ (64 * mb);
 
-  // S^T of one tile: K rows are the A operand (LDS), q^T the B operand.
-  auto qk = [&](const char* kt, f32x16& s) {
+  // S^T of one tile for every block: K rows are the A operand (LDS, one read
+  // per step for all blocks), q^T the B operand.
+  auto qk = [&](const char* kt, f32x16 (&s)[RB]) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[rb][i] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const u32x4 kf = *reinterpret_cast<const u32x4*>(kt + ka[kk]);
-      s = T::mfma_32x32x16(kf, qv[kk], s);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) s[rb] = T::mfma_32x32x16(kf, qv[rb][kk], s[rb]);
     }
   };
   // Masks tile ti's scores where the tile reaches past k1 or past the row's
   // causal limit (wave-uniform test; one compare and select per score).
-  auto mask = [&](int ti, f32x16& s) {
+  auto mask = [&](int ti, f32x16 (&s)[RB]) {
     const int tb = k0 + ti * KT;
     if constexpr (VAR) {
       if (capped) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = soft_cap(s[i], a.var.cap_in, a.var.cap_out);
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[rb][i] = soft_cap(s[rb][i], a.var.cap_in, a.var.cap_out);
       }
       if (tb + KT - 1 > mask_from || tb < win_from) {
-        const int tlast = (a.causal ? min(k1 - 1, lim) : k1 - 1) - (tb + 4 * half);
-        const int tfirst = wlo - (tb + 4 * half);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int off = 8 * (i >> 2) + (i & 3);
-          if (off > tlast || off < tfirst) s[i] = neg_inf();
+        for (int rb = 0; rb < RB; ++rb) {
+          const int tlast = (a.causal ? min(k1 - 1, lim[rb]) : k1 - 1) - (tb + 4 * half);
+          const int tfirst = wlo[rb] - (tb + 4 * half);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int off = 8 * (i >> 2) + (i & 3);
+            if (off > tlast || off < tfirst) s[rb][i] = neg_inf();
+          }
         }
       }
     } else if (tb + KT - 1 > mask_from) {
-      const int tlast = (a.causal ? min(k1 - 1, lim) : k1 - 1) - (tb + 4 * half);
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (8 * (i >> 2) + (i & 3) > tlast) s[i] = neg_inf();
+      for (int rb = 0; rb < RB; ++rb) {
+        const int tlast = (a.causal ? min(k1 - 1, lim[rb]) : k1 - 1) - (tb + 4 * half);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (8 * (i >> 2) + (i & 3) > tlast) s[rb][i] = neg_inf();
+      }
     }
   };
   // Largest raw score this lane holds of a tile (half of its row's keys).
@@ -389,44 +428,47 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
     for (int i = 0; i < 16; ++i) t = fmaxf(t, s[i]);
     return t;
   };
-  // Moves the reference where some lane's scores outgrew the threshold
+  // Moves block rb's reference where some lane's scores outgrew the threshold
   // (wave-uniform branch): every row takes its full maximum over both halves,
-  // and O and the sum are rescaled by the same factor.
-  auto maybe_rescale = [&](float lmax) {
-    if (__builtin_amdgcn_ballot_w64(lmax > thr) != 0) {
-      const float m_new = fmaxf(m_ref, max_across_halves(lmax) * a.scale_log2);
-      const float alpha = (m_new == neg_inf()) ? 1.f : fast_exp2(m_ref - m_new);
-      m_ref = m_new;
-      neg_m = (m_new == neg_inf()) ? 0.f : -m_new;
-      thr = (m_new == neg_inf()) ? neg_inf() : (m_new + kRescaleSlack) * inv_scale_log2;
-      l_run *= alpha;
-      if constexpr (kExactLse) l_lse *= alpha;
+  // and O and the sums are rescaled by the same factor.
+  auto maybe_rescale = [&](int rb, float lmax) {
+    if (__builtin_amdgcn_ballot_w64(lmax > thr[rb]) != 0) {
+      const float m_new = fmaxf(m_ref[rb], max_across_halves(lmax) * a.scale_log2);
+      const float alpha = (m_new == neg_inf()) ? 1.f : fast_exp2(m_ref[rb] - m_new);
+      m_ref[rb] = m_new;
+      neg_m[rb] = (m_new == neg_inf()) ? 0.f : -m_new;
+      thr[rb] = (m_new == neg_inf()) ? neg_inf() : (m_new + kRescaleSlack) * inv_scale_log2;
+      l_run[rb] *= alpha;
+      if constexpr (kExactLse) l_lse[rb] *= alpha;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) acc[mb] *= alpha;
+      for (int mb = 0; mb < 4; ++mb) acc[rb][mb] *= alpha;
     }
   };
-  // Weights of a tile, rounded to the storage dtype: pk[st] is the B operand
-  // of 16-token step st of the PV product.
-  auto weights = [&](const f32x16& s, u32x4 (&pk)[2]) {
-    float sum = l_run, xsum = l_lse;
+  // Weights of a tile, rounded to the storage dtype: pk[rb][st] is the B
+  // operand of 16-token step st of block rb's PV product.
+  auto weights = [&](const f32x16 (&s)[RB], u32x4 (&pk)[RB][2]) {
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int rb = 0; rb < RB; ++rb) {
+      float sum = l_run[rb], xsum = l_lse[rb];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x0 = fast_exp2(fmaf(s[8 * st + 2 * j], a.scale_log2, neg_m));
-        const float x1 = fast_exp2(fmaf(s[8 * st + 2 * j + 1], a.scale_log2, neg_m));
-        pk[st][j] = T::pack2(x0, x1);
-        sum = T::add_pair(pk[st][j], sum);
-        if constexpr (kExactLse) xsum += x0 + x1;
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float x0 = fast_exp2(fmaf(s[rb][8 * st + 2 * j], a.scale_log2, neg_m[rb]));
+          const float x1 = fast_exp2(fmaf(s[rb][8 * st + 2 * j + 1], a.scale_log2, neg_m[rb]));
+          pk[rb][st][j] = T::pack2(x0, x1);
+          sum = T::add_pair(pk[rb][st][j], sum);
+          if constexpr (kExactLse) xsum += x0 + x1;
+        }
       }
+      l_run[rb] = sum;
+      l_lse[rb] = xsum;
     }
-    l_run = sum;
-    l_lse = xsum;
   };
   // O^T += V^T P^T over two 16-token steps. Step st covers tokens
   // 16st + 4*half + {0..3} (first read) and + {8..11} (second read), the
-  // order in which pk[st] holds them.
-  auto pv = [&](const char* vt, const u32x4 (&pk)[2]) {
+  // order in which pk[rb][st] holds them.
+  auto pv = [&](const char* vt, const u32x4 (&pk)[RB][2]) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
@@ -435,15 +477,18 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
         const s16x4 lo = lds_read_tr16_b64(p);
         const s16x4 hi = lds_read_tr16_b64(p + 8 * kRowBytes);
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        acc[mb] = T::mfma_32x32x16(u32x4{l2[0], l2[1], h2[0], h2[1]}, pk[st], acc[mb]);
+        const u32x4 vfr = u32x4{l2[0], l2[1], h2[0], h2[1]};
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acc[rb][mb] = T::mfma_32x32x16(vfr, pk[rb][st], acc[rb][mb]);
       }
     }
   };
 
   // The two halves of a pipelined iteration. The instruction order is written
-  // out: each step issues an LDS read two MFMAs ahead of its use, one MFMA,
-  // and a slice of the VALU work of the other tile, and a scheduling fence
-  // (sched_barrier) keeps the compiler from regrouping the steps.
+  // out: each step issues an LDS read two MFMA steps ahead of its use, one MFMA
+  // per block, and a slice of the VALU work of the other tile, and a
+  // scheduling fence (sched_barrier) keeps the compiler from regrouping the
+  // steps.
   auto k_read = [&](const char* kt, int kk) -> u32x4 {
     return *reinterpret_cast<const u32x4*>(kt + ka[kk]);
   };
@@ -453,61 +498,80 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
     const u32x2 hi = __builtin_bit_cast(u32x2, lds_read_tr16_b64(p + 8 * kRowBytes));
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
   };
-  // S(j+1) (8 MFMAs over d) with the weights of tile j, one pair of scores
-  // per MFMA; kf[0..1] hold the first two K operands on entry. The last two
-  // steps read the first two V operands of the PV product into vf[0..1].
-  // The weight work is skewed over three steps so that no instruction waits
-  // for a result of its own step: step kk takes the exponentials of pair kk
-  // (arguments formed one step earlier), forms the arguments of pair kk+1,
-  // and packs and sums pair kk-1. The empty asm statements keep the sums in
-  // their step (otherwise the compiler sinks them into one dependent chain
-  // in front of the PV product).
-  auto qk_weights = [&](const char* kt, u32x4 (&kf)[3], f32x16& s, const f32x16& sc,
-                        u32x4 (&pk)[2], const char* vt, u32x4 (&vf)[3]) {
-    float sum = l_run, xsum = l_lse;
-    float a0 = fmaf(sc[0], a.scale_log2, neg_m), a1 = fmaf(sc[1], a.scale_log2, neg_m);
-    float x0p = 0.f, x1p = 0.f;
+  // S(j+1) (8 MFMA steps over d) with the weights of tile j, one pair of
+  // scores per block and step; kf[0..1] hold the first two K operands on
+  // entry. The last two steps read the first two V operands of the PV product
+  // into vf[0..1]. The weight work is skewed over three steps so that no
+  // instruction waits for a result of its own step: step kk takes the
+  // exponentials of pair kk (arguments formed one step earlier), forms the
+  // arguments of pair kk+1, and packs and sums pair kk-1. The empty asm
+  // statements keep the sums in their step (otherwise the compiler sinks them
+  // into one dependent chain in front of the PV product).
+  auto qk_weights = [&](const char* kt, u32x4 (&kf)[3], f32x16 (&s)[RB], const f32x16 (&sc)[RB],
+                        u32x4 (&pk)[RB][2], const char* vt, u32x4 (&vf)[3]) {
+    float sum[RB], xsum[RB], a0[RB], a1[RB], x0p[RB], x1p[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      sum[rb] = l_run[rb];
+      xsum[rb] = l_lse[rb];
+      a0[rb] = fmaf(sc[rb][0], a.scale_log2, neg_m[rb]);
+      a1[rb] = fmaf(sc[rb][1], a.scale_log2, neg_m[rb]);
+      x0p[rb] = x1p[rb] = 0.f;
+    }
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       if (kk + 2 < 8) kf[(kk + 2) % 3] = k_read(kt, kk + 2);
       else vf[kk - 6] = v_read(vt, kk - 6);
-      s = T::mfma_32x32x16(kf[kk % 3], qv[kk], kk == 0 ? f32x16{} : s);
-      const float x0 = fast_exp2(a0), x1 = fast_exp2(a1);
-      if (kk + 1 < 8) {
-        a0 = fmaf(sc[2 * kk + 2], a.scale_log2, neg_m);
-        a1 = fmaf(sc[2 * kk + 3], a.scale_log2, neg_m);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        s[rb] = T::mfma_32x32x16(kf[kk % 3], qv[rb][kk], kk == 0 ? f32x16{} : s[rb]);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float x0 = fast_exp2(a0[rb]), x1 = fast_exp2(a1[rb]);
+        if (kk + 1 < 8) {
+          a0[rb] = fmaf(sc[rb][2 * kk + 2], a.scale_log2, neg_m[rb]);
+          a1[rb] = fmaf(sc[rb][2 * kk + 3], a.scale_log2, neg_m[rb]);
+        }
+        if (kk > 0) {
+          pk[rb][(kk - 1) >> 2][(kk - 1) & 3] = T::pack2(x0p[rb], x1p[rb]);
+          sum[rb] = T::add_pair(pk[rb][(kk - 1) >> 2][(kk - 1) & 3], sum[rb]);
+          if constexpr (kExactLse) xsum[rb] += x0p[rb] + x1p[rb];
+          asm volatile("" : "+v"(sum[rb]));
+          if constexpr (kExactLse) asm volatile("" : "+v"(xsum[rb]));
+        }
+        x0p[rb] = x0;
+        x1p[rb] = x1;
       }
-      if (kk > 0) {
-        pk[(kk - 1) >> 2][(kk - 1) & 3] = T::pack2(x0p, x1p);
-        sum = T::add_pair(pk[(kk - 1) >> 2][(kk - 1) & 3], sum);
-        if constexpr (kExactLse) xsum += x0p + x1p;
-        asm volatile("" : "+v"(sum));
-        if constexpr (kExactLse) asm volatile("" : "+v"(xsum));
-      }
-      x0p = x0;
-      x1p = x1;
       __builtin_amdgcn_sched_barrier(0);
     }
-    pk[1][3] = T::pack2(x0p, x1p);
-    sum = T::add_pair(pk[1][3], sum);
-    if constexpr (kExactLse) xsum += x0p + x1p;
-    l_run = sum;
-    l_lse = xsum;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      pk[rb][1][3] = T::pack2(x0p[rb], x1p[rb]);
+      sum[rb] = T::add_pair(pk[rb][1][3], sum[rb]);
+      if constexpr (kExactLse) xsum[rb] += x0p[rb] + x1p[rb];
+      l_run[rb] = sum[rb];
+      l_lse[rb] = xsum[rb];
+    }
   };
-  // PV of tile j (8 MFMAs) with the lane maxima of tile j+1's scores, one
-  // pair per MFMA; returns the lane maximum (raw scores).
-  auto pv_max = [&](const char* vt, u32x4 (&vf)[3], const u32x4 (&pk)[2],
-                    const f32x16& sn) -> float {
-    float t = neg_inf();
+  // PV of tile j (8 MFMA steps) with the lane maxima of tile j+1's scores, one
+  // pair per block and step; leaves the lane maxima (raw scores) in t.
+  auto pv_max = [&](const char* vt, u32x4 (&vf)[3], const u32x4 (&pk)[RB][2],
+                    const f32x16 (&sn)[RB], float (&t)[RB]) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) t[rb] = neg_inf();
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (i + 2 < 8) vf[(i + 2) % 3] = v_read(vt, i + 2);
-      acc[i & 3] = T::mfma_32x32x16(vf[i % 3], pk[i >> 2], acc[i & 3]);
-      t = fmaxf(fmaxf(t, sn[2 * i]), sn[2 * i + 1]);
-      asm volatile("" : "+v"(t));   // likewise for the running maximum
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        acc[rb][i & 3] = T::mfma_32x32x16(vf[i % 3], pk[rb][i >> 2], acc[rb][i & 3]);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        t[rb] = fmaxf(fmaxf(t[rb], sn[rb][2 * i]), sn[rb][2 * i + 1]);
+        asm volatile("" : "+v"(t[rb]));   // likewise for the running maxima
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    return t;
   };
 
   // Software pipeline over KV tiles. Iteration j: the loads of K(j+4) and
@@ -524,7 +588,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
   Pids pid_k0, pid_k1, pid_v;
   Group grp_v{0, 0};   // uniform mode: where the V load of tile j+3 reads
   // `ph` is j % 4 as a compile-time constant, so buffer choices are constants.
-  auto body = [&](int j, auto ph, f32x16& s_cur, f32x16& s_nxt, bool has_next) {
+  auto body = [&](int j, auto ph, f32x16 (&s_cur)[RB], f32x16 (&s_nxt)[RB], bool has_next) {
     constexpr int p = decltype(ph)::value;
     char* kn = kbuf(std::integral_constant<int, p>{});                  // receives K(j+4)
     char* vn = vbuf(std::integral_constant<int, (p + 3) & 3>{});        // receives V(j+3)
@@ -549,13 +613,17 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
     pid_k0 = pid_k1;
     pid_k1 = pnn;
 
-    u32x4 pk[2];
+    u32x4 pk[RB][2];
     if (has_next) {
       qk_weights(kt, kf, s_nxt, s_cur, pk, vt, vf);
       // The weights are complete here (kept from sinking past the branch).
-      asm volatile("" ::"v"(pk[0]), "v"(pk[1]));
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) asm volatile("" ::"v"(pk[rb][0]), "v"(pk[rb][1]));
       mask(j + 1, s_nxt);
-      maybe_rescale(pv_max(vt, vf, pk, s_nxt));
+      float t[RB];
+      pv_max(vt, vf, pk, s_nxt, t);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) maybe_rescale(rb, t[rb]);
     } else {
       weights(s_cur, pk);
       pv(vt, pk);
@@ -588,10 +656,11 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
     wait_vm<2 * kLoadsPerIter>();
     lds_barrier();
 
-    f32x16 sA, sB;
+    f32x16 sA[RB], sB[RB];
     qk(sK0, sA);
     mask(0, sA);
-    maybe_rescale(lane_max(sA));
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) maybe_rescale(rb, lane_max(sA[rb]));
     // Every wave has read K(0) before iteration 0 refills its buffer.
     lds_barrier();
     constexpr std::integral_constant<int, 0> ph0{};
@@ -616,53 +685,57 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
     }
   }
 
-  // Finalize row lr.
-  float l_tot = sum_across_halves(l_run);
-  float l_ex = kExactLse ? sum_across_halves(l_lse) : l_tot;
-  if (!row_ok) return;
-  float o_scale = 1.f;   // factor on the accumulator besides 1 / l_tot
-  if constexpr (VAR) {
-    // The head's sink (log2 domain) is one more term of both sums, with a
-    // zero value: move the reference to the larger of the two and add it.
-    if (a.var.sinks != nullptr && slot < 0) {
-      const float sink = a.var.sinks[head] * kLog2e;
-      const float m_new = fmaxf(m_ref, sink);
-      if (m_new != neg_inf()) {
-        o_scale = fast_exp2(m_ref - m_new);
-        const float w_sink = fast_exp2(sink - m_new);
-        l_tot = l_tot * o_scale + w_sink;
-        l_ex = l_ex * o_scale + w_sink;
-        m_ref = m_new;
+  // Finalize each block's row lr.
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float l_tot = sum_across_halves(l_run[rb]);
+    float l_ex = kExactLse ? sum_across_halves(l_lse[rb]) : l_tot;
+    if (!row_ok[rb]) continue;
+    float m_fin = m_ref[rb];
+    float o_scale = 1.f;   // factor on the accumulator besides 1 / l_tot
+    if constexpr (VAR) {
+      // The head's sink (log2 domain) is one more term of both sums, with a
+      // zero value: move the reference to the larger of the two and add it.
+      if (a.var.sinks != nullptr && slot < 0) {
+        const float sink = a.var.sinks[head[rb]] * kLog2e;
+        const float m_new = fmaxf(m_fin, sink);
+        if (m_new != neg_inf()) {
+          o_scale = fast_exp2(m_fin - m_new);
+          const float w_sink = fast_exp2(sink - m_new);
+          l_tot = l_tot * o_scale + w_sink;
+          l_ex = l_ex * o_scale + w_sink;
+          m_fin = m_new;
+        }
       }
     }
-  }
-  const float inv = l_tot > 0.f ? o_scale / l_tot : 0.f;
-  const float lse = l_ex > 0.f ? (m_ref + fast_log2(l_ex)) * kLn2 : neg_inf();
-  if (slot < 0) {
-    const int64_t orow = static_cast<int64_t>(q0 + qtok) * a.num_qo_heads + head;
-    OUT* o = static_cast<OUT*>(a.o) + orow * D;
+    const float inv = l_tot > 0.f ? o_scale / l_tot : 0.f;
+    const float lse = l_ex > 0.f ? (m_fin + fast_log2(l_ex)) * kLn2 : neg_inf();
+    if (slot < 0) {
+      const int64_t orow = static_cast<int64_t>(q0 + qtok[rb]) * a.num_qo_heads + head[rb];
+      OUT* o = static_cast<OUT*>(a.o) + orow * D;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = 32 * mb + 8 * q4 + 4 * half;
-        store4<OUT>(o + d, acc[mb][4 * q4] * inv, acc[mb][4 * q4 + 1] * inv,
-                    acc[mb][4 * q4 + 2] * inv, acc[mb][4 * q4 + 3] * inv);
-      }
-    if (half == 0 && a.lse != nullptr) a.lse[orow] = lse;
-  } else {
-    const int64_t srow_out = static_cast<int64_t>(slot) * kTileRows + 32 * wave + lr;
-    float* po = a.part_o + srow_out * D;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d = 32 * mb + 8 * q4 + 4 * half;
+          store4<OUT>(o + d, acc[rb][mb][4 * q4] * inv, acc[rb][mb][4 * q4 + 1] * inv,
+                      acc[rb][mb][4 * q4 + 2] * inv, acc[rb][mb][4 * q4 + 3] * inv);
+        }
+      if (half == 0 && a.lse != nullptr) a.lse[orow] = lse;
+    } else {
+      const int64_t srow_out = static_cast<int64_t>(slot) * kRows + 32 * RB * wave + 32 * rb + lr;
+      float* po = a.part_o + srow_out * D;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = 32 * mb + 8 * q4 + 4 * half;
-        *reinterpret_cast<f32x4*>(po + d) =
-            f32x4{acc[mb][4 * q4] * inv, acc[mb][4 * q4 + 1] * inv, acc[mb][4 * q4 + 2] * inv,
-                  acc[mb][4 * q4 + 3] * inv};
-      }
-    if (half == 0) a.part_lse[srow_out] = lse;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d = 32 * mb + 8 * q4 + 4 * half;
+          *reinterpret_cast<f32x4*>(po + d) =
+              f32x4{acc[rb][mb][4 * q4] * inv, acc[rb][mb][4 * q4 + 1] * inv,
+                    acc[rb][mb][4 * q4 + 2] * inv, acc[rb][mb][4 * q4 + 3] * inv};
+        }
+      if (half == 0) a.part_lse[srow_out] = lse;
+    }
   }
 }
 
