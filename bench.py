@@ -11,7 +11,10 @@ Timing: W warm-up steps, then K timed steps. Before every step a 512 MiB
 buffer is read (outside the timed events) so the 256 MB Infinity Cache holds
 no KV and no dirty lines that would be written back during the step; each
 step is bracketed by HIP events on the stream the kernels run on.
-value = algorithmic bytes / mean step time.
+value = algorithmic bytes / mean step time. The attention kernel alone (the
+roofline figure) is timed by a second pair of events that its own dispatch
+carries (hipExtLaunchKernel), i.e. its begin and end timestamps, the same
+interval rocprofv3's kernel trace reports.
 
 `--workload` selects another workload (single, decode, prefill, cascade,
 long); `--all` adds every workload's figures under "workloads" in the line.
@@ -231,19 +234,23 @@ class Runner:
                                              w.num_kv_heads, w.head_dim, w.kv.page_size, dt,
                                              self.ws)
 
-    def step(self, attention_done=None):
-        """One run; `attention_done` (decode / prefill) is recorded after the attention
-        kernel, before the merge of split chunks."""
+    def step(self, kernel_events=None):
+        """One run; `kernel_events` (decode / prefill / mixed: a (start, done) pair of
+        torch.cuda.Events, or None) ride on the attention kernel's own dispatch and take
+        its begin and end timestamps (the merge of split chunks is not included)."""
         p, w = self.pkv, self.w
+        attention_start, attention_done = kernel_events or (None, None)
         if w.kind == "pod" and self.sequential:
             p.pkv_prefill_run(self.plan_p, self.q_p, self.k, self.v, self.qo, self.ip, self.ix,
                               w.prefill.sm_scale, o=self.o_p, lse=self.l_p)
             p.pkv_decode_run_timed(self.plan_d, self.q_d, self.k, self.v, self.dp, self.dx,
-                                   w.decode.sm_scale, attention_done, o=self.o_d, lse=self.l_d)
+                                   w.decode.sm_scale, attention_start, attention_done,
+                                   o=self.o_d, lse=self.l_d)
         elif w.kind == "pod":
             p.pkv_pod_run(self.plan, self.k, self.v, self.q_p, self.qo, self.ip, self.ix, self.q_d,
                           self.dp, self.dx, w.prefill.sm_scale, o_p=self.o_p, lse_p=self.l_p,
-                          o_d=self.o_d, lse_d=self.l_d, attention_done=attention_done)
+                          o_d=self.o_d, lse_d=self.l_d, attention_start=attention_start,
+                          attention_done=attention_done)
         elif w.kind == "block_sparse":
             p.pkv_block_sparse_run(self.plan, self.q, self.k, self.v, self.ip, self.ix,
                                    w.sm_scale, o=self.o, lse=self.lse)
@@ -255,14 +262,16 @@ class Runner:
                                 lse=self.lse)
         elif w.kind == "decode":
             p.pkv_decode_run_timed(self.plan, self.q, self.k, self.v, self.kv_indptr,
-                                   self.kv_indices, w.sm_scale, attention_done, o=self.o,
+                                   self.kv_indices, w.sm_scale, attention_start, attention_done,
+                                   o=self.o,
                                    lse=self.lse, window_left=self.window_left,
                                    logits_soft_cap=self.soft_cap, sinks=self.sinks)
         elif w.kind == "prefill":
             p.pkv_prefill_run_timed(self.plan, self.q, self.k, self.v, self.qo_indptr,
-                                    self.kv_indptr, self.kv_indices, w.sm_scale, attention_done,
-                                    o=self.o, lse=self.lse, window_left=self.window_left,
-                                    logits_soft_cap=self.soft_cap, sinks=self.sinks)
+                                    self.kv_indptr, self.kv_indices, w.sm_scale, attention_start,
+                                    attention_done, o=self.o, lse=self.lse,
+                                    window_left=self.window_left, logits_soft_cap=self.soft_cap,
+                                    sinks=self.sinks)
         else:
             p.pkv_cascade_run(self.plan, self.q, self.k, self.v, self.prefix, self.kv_indptr,
                               self.kv_indices, w.sm_scale, o=self.o, lse=self.lse)
@@ -324,27 +333,32 @@ def time_steps(torch, runner, steps, warmup, flush):
         return flush.view(torch.int64).sum()
 
     timed_kernel = runner.w.kind in ("decode", "prefill", "pod")
+
+    def event():
+        return torch.cuda.Event(enable_timing=True)
     for _ in range(warmup):
         evict()
-        runner.step(torch.cuda.Event(enable_timing=True) if timed_kernel else None)
+        runner.step((event(), event()) if timed_kernel else None)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    mids = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    for ev in mids:                          # create the events before the timed loop
+    starts = [event() for _ in range(steps)]
+    ends = [event() for _ in range(steps)]
+    # The attention kernel's own begin / end timestamps (events carried by its dispatch).
+    k_begin = [event() for _ in range(steps)]
+    k_end = [event() for _ in range(steps)]
+    for ev in k_begin + k_end:               # create the events before the timed loop
         ev.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         evict()                              # evicts the Infinity Cache, outside the events
         starts[i].record(stream)
-        runner.step(mids[i] if timed_kernel else None)
+        runner.step((k_begin[i], k_end[i]) if timed_kernel else None)
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    kern = [s.elapsed_time(m) for s, m in zip(starts, mids)] if timed_kernel else None
+    kern = [b.elapsed_time(e) for b, e in zip(k_begin, k_end)] if timed_kernel else None
     return (float(np.mean(ms)), float(np.median(ms)),
             float(np.mean(kern)) if kern else None, wall)
 
@@ -502,7 +516,7 @@ def main():
                                 "logit soft cap 50, sinks",
         }[name], "head_dim": 128, "tokens_per_step": r.work()[2],
             "tokens_per_s": res["tokens_per_s"], "plan_us": res["plan_us"]},
-        # the dominant kernel (the attention kernel, timed alone with events)
+        # the dominant kernel (the attention kernel, timed by the events its dispatch carries)
         "roofline": {
             "bound": "mfma" if prefill_like else "hbm",
             "achieved": res["kernel_TFLOPs"] if prefill_like else res["kernel_GBps"],

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 2
+#define PKV_ABI_VERSION 3
 
 typedef int32_t pkv_status;
 enum {
@@ -266,14 +266,16 @@ pkv_status pkv_decode_run(const pkv_plan_info* plan, const void* q, const pkv_pa
                           float sm_scale, const pkv_variant* variant, void* o, float* lse,
                           void* stream);
 
-/* As pkv_decode_run, and records `attention_done` (a hipEvent_t passed as
- * void*, created by the caller; NULL = none) on `stream` right after the
- * attention kernel and before the merge of split chunks, so a caller can time
- * the two kernels separately. */
+/* As pkv_decode_run, and times the attention kernel: `attention_start` and
+ * `attention_done` (hipEvent_t passed as void*, created by the caller; either
+ * may be NULL) ride on the attention kernel's own dispatch (hipExtLaunchKernel),
+ * taking its begin and end timestamps, so hipEventElapsedTime between them is
+ * that kernel's run time alone (not the queue's dispatch latency, not the
+ * merge of split chunks that follows). */
 pkv_status pkv_decode_run_timed(const pkv_plan_info* plan, const void* q, const pkv_paged_kv* kv,
                                 const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
                                 float sm_scale, const pkv_variant* variant, void* o, float* lse,
-                                void* stream, void* attention_done);
+                                void* stream, void* attention_start, void* attention_done);
 
 /* ---------------------------------------------------------------------------
  * Batch paged prefill / append: Q_b = qo_indptr[b+1]-qo_indptr[b] query
@@ -296,13 +298,13 @@ pkv_status pkv_prefill_run(const pkv_plan_info* plan, const void* q, const pkv_p
                            const int32_t* kv_indices_d, float sm_scale,
                            const pkv_variant* variant, void* o, float* lse, void* stream);
 
-/* As pkv_prefill_run, recording `attention_done` after the attention kernel
- * (see pkv_decode_run_timed). */
+/* As pkv_prefill_run, with `attention_start` / `attention_done` on the
+ * attention kernel's dispatch (see pkv_decode_run_timed). */
 pkv_status pkv_prefill_run_timed(const pkv_plan_info* plan, const void* q, const pkv_paged_kv* kv,
                                  const int32_t* qo_indptr_d, const int32_t* kv_indptr_d,
                                  const int32_t* kv_indices_d, float sm_scale,
                                  const pkv_variant* variant, void* o, float* lse, void* stream,
-                                 void* attention_done);
+                                 void* attention_start, void* attention_done);
 
 /* ---------------------------------------------------------------------------
  * Single-request decode over a contiguous NHD cache k, v [kv_len, Hkv, 128]
@@ -440,14 +442,15 @@ pkv_status pkv_pod_run(const pkv_plan_info* plan, const pkv_paged_kv* kv, const 
                        const int32_t* kv_indptr_d_d, const int32_t* kv_indices_d_d, void* o_d,
                        float* lse_d, float sm_scale, void* stream);
 
-/* As pkv_pod_run, recording `attention_done` after the mixed kernel (before
- * the merges; see pkv_decode_run_timed). */
+/* As pkv_pod_run, with `attention_start` / `attention_done` on the mixed
+ * kernel's dispatch (the merges are not included; see pkv_decode_run_timed). */
 pkv_status pkv_pod_run_timed(const pkv_plan_info* plan, const pkv_paged_kv* kv, const void* q_p,
                              const int32_t* qo_indptr_d, const int32_t* kv_indptr_p_d,
                              const int32_t* kv_indices_p_d, void* o_p, float* lse_p,
                              const void* q_d, const int32_t* kv_indptr_d_d,
                              const int32_t* kv_indices_d_d, void* o_d, float* lse_d,
-                             float sm_scale, void* stream, void* attention_done);
+                             float sm_scale, void* stream, void* attention_start,
+                             void* attention_done);
 
 /* ---------------------------------------------------------------------------
  * Appending new K/V rows into a paged cache (docs index "flashinfer.page" >

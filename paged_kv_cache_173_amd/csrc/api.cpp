@@ -392,20 +392,24 @@ pkv_status merge_part(const pkv_plan_part& part, bool prefill, const int32_t* qo
   return PKV_OK;
 }
 
+// The caller's timing events (hipEvent_t passed as void*, either may be NULL),
+// carried by the attention kernel's own dispatch.
+pkv::LaunchEvents launch_events(void* start, void* stop) {
+  return {static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop)};
+}
+
 // Launches one decode pass (items + merge) writing final rows to o / lse.
 pkv_status run_decode_part(const pkv_plan_info* plan, const pkv_plan_part& part, const void* q,
                            const pkv_paged_kv* kv, const int32_t* kv_indptr_d,
                            const int32_t* kv_indices_d, float sm_scale, void* o, float* lse,
                            pkv::OutKind out_kind, hipStream_t stream,
-                           hipEvent_t attention_done = nullptr,
+                           const pkv::LaunchEvents& ev = {},
                            const pkv::VariantArgs& var = kNoVariant) {
   const pkv::DecodeArgs a =
       decode_args(plan, part, q, kv, kv_indptr_d, kv_indices_d, sm_scale, o, lse, var);
-  hipError_t e = pkv::launch_decode(a, plan->dtype, out_kind, page_mode(plan->page_size),
-                                    part.num_items, stream);
+  const hipError_t e = pkv::launch_decode(a, plan->dtype, out_kind, page_mode(plan->page_size),
+                                          part.num_items, stream, ev);
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
-  if (attention_done != nullptr && (e = hipEventRecord(attention_done, stream)) != hipSuccess)
-    return hip_fail(e, "hipEventRecord");
   return merge_part(part, false, nullptr, plan->num_qo_heads, a.group, plan->int_ws,
                     plan->float_ws, o, lse, var.sinks, plan->dtype, out_kind, stream);
 }
@@ -415,15 +419,13 @@ pkv_status run_prefill_part(const pkv_plan_info* plan, const pkv_plan_part& part
                             const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
                             float sm_scale, void* o, float* lse, int32_t num_qo_heads,
                             pkv::OutKind out_kind, hipStream_t stream,
-                            hipEvent_t attention_done = nullptr,
+                            const pkv::LaunchEvents& ev = {},
                             const pkv::VariantArgs& var = kNoVariant) {
   const pkv::PrefillArgs a = prefill_args(plan, part, q, kv, qo_indptr_d, kv_indptr_d,
                                           kv_indices_d, sm_scale, o, lse, num_qo_heads, var);
-  hipError_t e = pkv::launch_prefill(a, plan->dtype, out_kind, page_mode(plan->page_size),
-                                     part.num_items, stream);
+  const hipError_t e = pkv::launch_prefill(a, plan->dtype, out_kind, page_mode(plan->page_size),
+                                           part.num_items, stream, ev);
   if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
-  if (attention_done != nullptr && (e = hipEventRecord(attention_done, stream)) != hipSuccess)
-    return hip_fail(e, "hipEventRecord");
   return merge_part(part, true, qo_indptr_d, num_qo_heads, a.group, plan->int_ws, plan->float_ws,
                     o, lse, var.sinks, plan->dtype, out_kind, stream);
 }
@@ -563,13 +565,13 @@ pkv_status pkv_decode_run(const pkv_plan_info* plan, const void* q, const pkv_pa
                           float sm_scale, const pkv_variant* variant, void* o, float* lse,
                           void* stream) {
   return pkv_decode_run_timed(plan, q, kv, kv_indptr_d, kv_indices_d, sm_scale, variant, o, lse,
-                              stream, nullptr);
+                              stream, nullptr, nullptr);
 }
 
 pkv_status pkv_decode_run_timed(const pkv_plan_info* plan, const void* q, const pkv_paged_kv* kv,
                                 const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
                                 float sm_scale, const pkv_variant* variant, void* o, float* lse,
-                                void* stream, void* attention_done) {
+                                void* stream, void* attention_start, void* attention_done) {
   pkv_status st;
   if ((st = check_scale(sm_scale))) return st;
   if ((st = check_plan(plan, PKV_KIND_DECODE))) return st;
@@ -582,7 +584,7 @@ pkv_status pkv_decode_run_timed(const pkv_plan_info* plan, const void* q, const 
   if (!aligned16(q) || !aligned16(o)) return fail(PKV_ERR_INVALID_ARG, "q / o must be 16-byte aligned");
   if ((st = run_decode_part(plan, plan->part[0], q, kv, kv_indptr_d, kv_indices_d, sm_scale, o,
                             lse, pkv::kOutStorage, static_cast<hipStream_t>(stream),
-                            static_cast<hipEvent_t>(attention_done), var)))
+                            launch_events(attention_start, attention_done), var)))
     return st;
   return ok();
 }
@@ -636,14 +638,14 @@ pkv_status pkv_prefill_run(const pkv_plan_info* plan, const void* q, const pkv_p
                            const int32_t* kv_indices_d, float sm_scale,
                            const pkv_variant* variant, void* o, float* lse, void* stream) {
   return pkv_prefill_run_timed(plan, q, kv, qo_indptr_d, kv_indptr_d, kv_indices_d, sm_scale,
-                               variant, o, lse, stream, nullptr);
+                               variant, o, lse, stream, nullptr, nullptr);
 }
 
 pkv_status pkv_prefill_run_timed(const pkv_plan_info* plan, const void* q, const pkv_paged_kv* kv,
                                  const int32_t* qo_indptr_d, const int32_t* kv_indptr_d,
                                  const int32_t* kv_indices_d, float sm_scale,
                                  const pkv_variant* variant, void* o, float* lse, void* stream,
-                                 void* attention_done) {
+                                 void* attention_start, void* attention_done) {
   pkv_status st;
   if ((st = check_scale(sm_scale))) return st;
   if ((st = check_plan(plan, PKV_KIND_PREFILL))) return st;
@@ -657,7 +659,7 @@ pkv_status pkv_prefill_run_timed(const pkv_plan_info* plan, const void* q, const
   if ((st = run_prefill_part(plan, plan->part[0], q, kv, qo_indptr_d, kv_indptr_d, kv_indices_d,
                              sm_scale, o, lse, plan->num_qo_heads, pkv::kOutStorage,
                              static_cast<hipStream_t>(stream),
-                             static_cast<hipEvent_t>(attention_done), var)))
+                             launch_events(attention_start, attention_done), var)))
     return st;
   return ok();
 }
@@ -958,7 +960,7 @@ pkv_status pkv_pod_run(const pkv_plan_info* plan, const pkv_paged_kv* kv, const 
                        float* lse_d, float sm_scale, void* stream) {
   return pkv_pod_run_timed(plan, kv, q_p, qo_indptr_d, kv_indptr_p_d, kv_indices_p_d, o_p, lse_p,
                            q_d, kv_indptr_d_d, kv_indices_d_d, o_d, lse_d, sm_scale, stream,
-                           nullptr);
+                           nullptr, nullptr);
 }
 
 pkv_status pkv_pod_run_timed(const pkv_plan_info* plan, const pkv_paged_kv* kv, const void* q_p,
@@ -966,7 +968,8 @@ pkv_status pkv_pod_run_timed(const pkv_plan_info* plan, const pkv_paged_kv* kv, 
                              const int32_t* kv_indices_p_d, void* o_p, float* lse_p,
                              const void* q_d, const int32_t* kv_indptr_d_d,
                              const int32_t* kv_indices_d_d, void* o_d, float* lse_d,
-                             float sm_scale, void* stream, void* attention_done) {
+                             float sm_scale, void* stream, void* attention_start,
+                             void* attention_done) {
   pkv_status st;
   if ((st = check_scale(sm_scale))) return st;
   if ((st = check_plan(plan, PKV_KIND_POD))) return st;
@@ -986,11 +989,9 @@ pkv_status pkv_pod_run_timed(const pkv_plan_info* plan, const pkv_paged_kv* kv, 
   a.d = decode_args(plan, plan->part[1], q_d, kv, kv_indptr_d_d, kv_indices_d_d, sm_scale, o_d,
                     lse_d, kNoVariant);
   a.order = i_at(plan->int_ws, plan->order_off);
-  hipError_t e = pkv::launch_pod(a, plan->dtype, page_mode(plan->page_size), plan->num_blocks, s);
+  const hipError_t e = pkv::launch_pod(a, plan->dtype, page_mode(plan->page_size), plan->num_blocks,
+                                       s, launch_events(attention_start, attention_done));
   if (e != hipSuccess) return hip_fail(e, "mixed prefill + decode kernel launch");
-  if (attention_done != nullptr &&
-      (e = hipEventRecord(static_cast<hipEvent_t>(attention_done), s)) != hipSuccess)
-    return hip_fail(e, "hipEventRecord");
   if ((st = merge_part(plan->part[0], true, qo_indptr_d, plan->num_qo_heads, a.p.group,
                        plan->int_ws, plan->float_ws, o_p, lse_p, nullptr, plan->dtype,
                        pkv::kOutStorage, s)))

@@ -1,5 +1,7 @@
 // Paged decode kernel for gfx950: one work item (request, KV head, token
 // range) per workgroup; the item's computation is decode_item (decode_item.h).
+#include <hip/hip_ext.h>
+
 #include "decode_item.h"
 
 namespace pkv {
@@ -34,24 +36,25 @@ __global__ __launch_bounds__(256, 3) void decode_kernel(const DecodeArgs a) {
 }
 
 template <class T, class OUT>
-hipError_t launch_decode_t(const DecodeArgs& a, PageMode mode, int32_t grid, hipStream_t s) {
+hipError_t launch_decode_t(const DecodeArgs& a, PageMode mode, int32_t grid, hipStream_t s,
+                           const LaunchEvents& ev) {
   if (variant_on(a.var)) {
     if (mode == kContiguous) return hipErrorInvalidValue;
     if (mode == kPagedUniform)
-      hipLaunchKernelGGL((decode_kernel<T, OUT, kPagedUniform, true>), dim3(grid), dim3(256), 0, s, a);
+      hipExtLaunchKernelGGL((decode_kernel<T, OUT, kPagedUniform, true>), dim3(grid), dim3(256), 0, s, ev.start, ev.stop, 0, a);
     else
-      hipLaunchKernelGGL((decode_kernel<T, OUT, kPagedGeneric, true>), dim3(grid), dim3(256), 0, s, a);
+      hipExtLaunchKernelGGL((decode_kernel<T, OUT, kPagedGeneric, true>), dim3(grid), dim3(256), 0, s, ev.start, ev.stop, 0, a);
     return hipGetLastError();
   }
   switch (mode) {
     case kContiguous:
-      hipLaunchKernelGGL((decode_kernel<T, OUT, kContiguous, false>), dim3(grid), dim3(256), 0, s, a);
+      hipExtLaunchKernelGGL((decode_kernel<T, OUT, kContiguous, false>), dim3(grid), dim3(256), 0, s, ev.start, ev.stop, 0, a);
       break;
     case kPagedUniform:
-      hipLaunchKernelGGL((decode_kernel<T, OUT, kPagedUniform, false>), dim3(grid), dim3(256), 0, s, a);
+      hipExtLaunchKernelGGL((decode_kernel<T, OUT, kPagedUniform, false>), dim3(grid), dim3(256), 0, s, ev.start, ev.stop, 0, a);
       break;
     default:
-      hipLaunchKernelGGL((decode_kernel<T, OUT, kPagedGeneric, false>), dim3(grid), dim3(256), 0, s, a);
+      hipExtLaunchKernelGGL((decode_kernel<T, OUT, kPagedGeneric, false>), dim3(grid), dim3(256), 0, s, ev.start, ev.stop, 0, a);
       break;
   }
   return hipGetLastError();
@@ -69,14 +72,14 @@ int32_t decode_occupancy() {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int32_t storage_dtype, OutKind out, PageMode mode,
-                         int32_t grid, hipStream_t stream) {
+                         int32_t grid, hipStream_t stream, const LaunchEvents& ev) {
   if (grid <= 0) return hipSuccess;
   if (storage_dtype == 0) {
-    return out == kOutF32 ? launch_decode_t<F16, float>(a, mode, grid, stream)
-                          : launch_decode_t<F16, _Float16>(a, mode, grid, stream);
+    return out == kOutF32 ? launch_decode_t<F16, float>(a, mode, grid, stream, ev)
+                          : launch_decode_t<F16, _Float16>(a, mode, grid, stream, ev);
   }
-  return out == kOutF32 ? launch_decode_t<BF16, float>(a, mode, grid, stream)
-                        : launch_decode_t<BF16, __bf16>(a, mode, grid, stream);
+  return out == kOutF32 ? launch_decode_t<BF16, float>(a, mode, grid, stream, ev)
+                        : launch_decode_t<BF16, __bf16>(a, mode, grid, stream, ev);
 }
 
 }  // namespace pkv

@@ -127,15 +127,26 @@ struct MergeGroupsArgs {
   const float* sinks;         // device [num_qo_heads] sink logits, or NULL
 };
 
+// Events a launch may carry on its own dispatch packet (hipExtLaunchKernel):
+// `start` takes the kernel's begin timestamp and `stop` its end timestamp, so
+// their elapsed time is the kernel's run time alone, without the queue's
+// dispatch latency. Either may be null.
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
 // Workgroups of the decode / prefill kernel resident per CU (0 on error).
 int32_t decode_occupancy();
 int32_t prefill_occupancy();
 
 hipError_t launch_decode(const DecodeArgs& a, int32_t storage_dtype, OutKind out,
-                         PageMode mode, int32_t grid, hipStream_t stream);
+                         PageMode mode, int32_t grid, hipStream_t stream,
+                         const LaunchEvents& ev = {});
 
 hipError_t launch_prefill(const PrefillArgs& a, int32_t storage_dtype, OutKind out,
-                          PageMode mode, int32_t grid, hipStream_t stream);
+                          PageMode mode, int32_t grid, hipStream_t stream,
+                          const LaunchEvents& ev = {});
 
 hipError_t launch_merge_groups(const MergeGroupsArgs& a, int32_t storage_dtype, OutKind out,
                                int32_t num_groups, hipStream_t stream);
@@ -144,7 +155,7 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 
 // Mixed prefill + decode launch; outputs are in the storage dtype.
 hipError_t launch_pod(const PodArgs& a, int32_t storage_dtype, PageMode mode, int32_t grid,
-                      hipStream_t stream);
+                      hipStream_t stream, const LaunchEvents& ev = {});
 
 // Public merges: v dtype in {F16, BF16, F32}; rows = n * H.
 hipError_t launch_merge2(const void* va, const float* sa, const void* vb, const float* sb,

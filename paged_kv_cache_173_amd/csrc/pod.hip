@@ -20,6 +20,8 @@
 // a decode item borrows the K tile buffers for its cross-wave merge
 // (16 x 128 floats = 8 KB per wave, one buffer each) and a V buffer for the
 // maxima and sums. No item uses both halves, so they never share LDS.
+#include <hip/hip_ext.h>
+
 #include "decode_item.h"
 #include "prefill_item.h"
 
@@ -47,24 +49,25 @@ __global__ __launch_bounds__(256, 2) void pod_kernel(const PodArgs a) {
 static_assert(16 * kHeadDim * sizeof(float) <= kTileBytes, "a wave's merge rows fit one tile buffer");
 
 template <class T>
-hipError_t launch_pod_t(const PodArgs& a, PageMode mode, int32_t grid, hipStream_t s) {
+hipError_t launch_pod_t(const PodArgs& a, PageMode mode, int32_t grid, hipStream_t s,
+                        const LaunchEvents& ev) {
   // Like the prefill launcher: the uniform kernel needs a power-of-two page.
   if (mode == kPagedUniform && (a.p.page_size & (a.p.page_size - 1)) != 0) mode = kPagedGeneric;
   if (mode == kPagedUniform)
-    hipLaunchKernelGGL((pod_kernel<T, kPagedUniform>), dim3(grid), dim3(256), 0, s, a);
+    hipExtLaunchKernelGGL((pod_kernel<T, kPagedUniform>), dim3(grid), dim3(256), 0, s, ev.start, ev.stop, 0, a);
   else
-    hipLaunchKernelGGL((pod_kernel<T, kPagedGeneric>), dim3(grid), dim3(256), 0, s, a);
+    hipExtLaunchKernelGGL((pod_kernel<T, kPagedGeneric>), dim3(grid), dim3(256), 0, s, ev.start, ev.stop, 0, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_pod(const PodArgs& a, int32_t storage_dtype, PageMode mode, int32_t grid,
-                      hipStream_t stream) {
+                      hipStream_t stream, const LaunchEvents& ev) {
   if (grid <= 0) return hipSuccess;
   if (mode == kContiguous) return hipErrorInvalidValue;
-  return storage_dtype == 0 ? launch_pod_t<F16>(a, mode, grid, stream)
-                            : launch_pod_t<BF16>(a, mode, grid, stream);
+  return storage_dtype == 0 ? launch_pod_t<F16>(a, mode, grid, stream, ev)
+                            : launch_pod_t<BF16>(a, mode, grid, stream, ev);
 }
 
 }  // namespace pkv

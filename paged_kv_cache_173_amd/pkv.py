@@ -101,10 +101,10 @@ _lib_decode_run = _sig("pkv_decode_run", _I32,
                         _F32, _VARP, _P, _P, _P])
 _lib_decode_run_timed = _sig("pkv_decode_run_timed", _I32,
                              [ctypes.POINTER(pkv_plan_info), _P, ctypes.POINTER(pkv_paged_kv), _P,
-                              _P, _F32, _VARP, _P, _P, _P, _P])
+                              _P, _F32, _VARP, _P, _P, _P, _P, _P])
 _lib_prefill_run_timed = _sig("pkv_prefill_run_timed", _I32,
                               [ctypes.POINTER(pkv_plan_info), _P, ctypes.POINTER(pkv_paged_kv), _P,
-                               _P, _P, _F32, _VARP, _P, _P, _P, _P])
+                               _P, _P, _F32, _VARP, _P, _P, _P, _P, _P])
 _lib_prefill_plan = _sig("pkv_prefill_plan", _I32,
                          [_I32P, _I32P, _I32P, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _VARP,
                           ctypes.POINTER(pkv_sched), _P, _SZ, _P, _SZ, _P, _SZ, _P,
@@ -146,7 +146,7 @@ _lib_pod_plan = _sig("pkv_pod_plan", _I32,
                       ctypes.POINTER(pkv_plan_info)])
 _lib_pod_run_timed = _sig("pkv_pod_run_timed", _I32,
                           [ctypes.POINTER(pkv_plan_info), ctypes.POINTER(pkv_paged_kv), _P, _P,
-                           _P, _P, _P, _P, _P, _P, _P, _P, _P, _F32, _P, _P])
+                           _P, _P, _P, _P, _P, _P, _P, _P, _P, _F32, _P, _P, _P])
 _lib_pod_run = _sig("pkv_pod_run", _I32,
                     [ctypes.POINTER(pkv_plan_info), ctypes.POINTER(pkv_paged_kv), _P, _P, _P, _P,
                      _P, _P, _P, _P, _P, _P, _P, _F32, _P])
@@ -364,10 +364,10 @@ def pkv_decode_run(plan: pkv_plan_info, q, k_cache, v_cache, kv_indptr_d, kv_ind
 
 
 def pkv_decode_run_timed(plan: pkv_plan_info, q, k_cache, v_cache, kv_indptr_d, kv_indices_d,
-                         sm_scale: float, attention_done, o=None, lse=None, stream=None,
-                         window_left=-1, logits_soft_cap=0.0, sinks=None):
-    """pkv_decode_run that records the torch.cuda.Event `attention_done` after the
-    attention kernel (before the merge)."""
+                         sm_scale: float, attention_start, attention_done, o=None, lse=None,
+                         stream=None, window_left=-1, logits_soft_cap=0.0, sinks=None):
+    """pkv_decode_run with the torch.cuda.Events `attention_start` / `attention_done`
+    (either may be None) taking the attention kernel's begin and end timestamps."""
     kv = paged_kv(k_cache, v_cache)
     q = q.contiguous()
     o = torch.empty_like(q) if o is None else o
@@ -375,7 +375,8 @@ def pkv_decode_run_timed(plan: pkv_plan_info, q, k_cache, v_cache, kv_indptr_d, 
     _check(_lib_decode_run_timed(ctypes.byref(plan), q.data_ptr(), ctypes.byref(kv),
                                  kv_indptr_d.data_ptr(), kv_indices_d.data_ptr(), float(sm_scale),
                                  _variant(window_left, logits_soft_cap, sinks), o.data_ptr(),
-                                 _ptr(lse), _stream(stream), _event(attention_done)),
+                                 _ptr(lse), _stream(stream), _event(attention_start),
+                                 _event(attention_done)),
            "pkv_decode_run_timed")
     return o, lse
 
@@ -412,9 +413,10 @@ def pkv_prefill_run(plan: pkv_plan_info, q, k_cache, v_cache, qo_indptr_d, kv_in
 
 
 def pkv_prefill_run_timed(plan: pkv_plan_info, q, k_cache, v_cache, qo_indptr_d, kv_indptr_d,
-                          kv_indices_d, sm_scale: float, attention_done, o=None, lse=None,
-                          stream=None, window_left=-1, logits_soft_cap=0.0, sinks=None):
-    """pkv_prefill_run that records `attention_done` after the attention kernel."""
+                          kv_indices_d, sm_scale: float, attention_start, attention_done, o=None,
+                          lse=None, stream=None, window_left=-1, logits_soft_cap=0.0, sinks=None):
+    """pkv_prefill_run with `attention_start` / `attention_done` on the attention kernel
+    (see pkv_decode_run_timed)."""
     kv = paged_kv(k_cache, v_cache)
     q = q.contiguous()
     o = torch.empty_like(q) if o is None else o
@@ -423,7 +425,8 @@ def pkv_prefill_run_timed(plan: pkv_plan_info, q, k_cache, v_cache, qo_indptr_d,
                                   qo_indptr_d.data_ptr(), kv_indptr_d.data_ptr(),
                                   kv_indices_d.data_ptr(), float(sm_scale),
                                   _variant(window_left, logits_soft_cap, sinks), o.data_ptr(),
-                                  _ptr(lse), _stream(stream), _event(attention_done)),
+                                  _ptr(lse), _stream(stream), _event(attention_start),
+                                  _event(attention_done)),
            "pkv_prefill_run_timed")
     return o, lse
 
@@ -533,9 +536,11 @@ def pkv_pod_host_order(plan: pkv_plan_info, host_ws) -> np.ndarray:
 
 def pkv_pod_run(plan: pkv_plan_info, k_cache, v_cache, q_p, qo_indptr_d, kv_indptr_p_d,
                 kv_indices_p_d, q_d, kv_indptr_d_d, kv_indices_d_d, sm_scale: float, o_p=None,
-                lse_p=None, o_d=None, lse_d=None, stream=None, attention_done=None):
-    """One launch for both parts -> (o_p, lse_p, o_d, lse_d); records the torch.cuda.Event
-    `attention_done` (if given) after the mixed kernel, before the merges."""
+                lse_p=None, o_d=None, lse_d=None, stream=None, attention_start=None,
+                attention_done=None):
+    """One launch for both parts -> (o_p, lse_p, o_d, lse_d); the torch.cuda.Events
+    `attention_start` / `attention_done` (if given) take the mixed kernel's begin and end
+    timestamps (the merges are not included)."""
     kv = paged_kv(k_cache, v_cache)
     q_p, q_d = q_p.contiguous(), q_d.contiguous()
     o_p = torch.empty_like(q_p) if o_p is None else o_p
@@ -547,10 +552,11 @@ def pkv_pod_run(plan: pkv_plan_info, k_cache, v_cache, q_p, qo_indptr_d, kv_indp
             kv_indptr_p_d.data_ptr(), kv_indices_p_d.data_ptr(), o_p.data_ptr(), _ptr(lse_p),
             q_d.data_ptr(), kv_indptr_d_d.data_ptr(), kv_indices_d_d.data_ptr(), o_d.data_ptr(),
             _ptr(lse_d), float(sm_scale), _stream(stream))
-    if attention_done is None:
+    if attention_start is None and attention_done is None:
         _check(_lib_pod_run(*args), "pkv_pod_run")
     else:
-        _check(_lib_pod_run_timed(*args, _event(attention_done)), "pkv_pod_run_timed")
+        _check(_lib_pod_run_timed(*args, _event(attention_start), _event(attention_done)),
+               "pkv_pod_run_timed")
     return o_p, lse_p, o_d, lse_d
 
 

@@ -27,7 +27,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_struct_size(lib):
-    assert lib.pkv_abi_version() == 2
+    assert lib.pkv_abi_version() == 3
     assert lib.pkv_plan_info_size() == ctypes.sizeof(lib.pkv_plan_info)
 
 
@@ -106,7 +106,7 @@ def test_run_rejects_foreign_or_mismatched_plans(lib):
     st, info = _decode_plan(lib, [0, 1], [1])
     assert st == lib.PKV_ERR_WORKSPACE_TOO_SMALL   # no workspaces given: header still filled
     info.magic = 0x31564B50
-    info.abi_version = 2
+    info.abi_version = lib.pkv_abi_version()
     info.kind = lib.PKV_KIND_DECODE
     info.page_size, info.num_kv_heads, info.head_dim, info.dtype = 16, 8, 128, 0
     kv.k = kv.v = 1 << 20
@@ -130,7 +130,7 @@ def _fake_decode_plan(lib, window_left=-1):
     st, info = _decode_plan(lib, [0, 1], [1], variant=lib.pkv_variant(window_left, 0.0, None))
     assert st == lib.PKV_ERR_WORKSPACE_TOO_SMALL
     info.magic = 0x31564B50
-    info.abi_version = 2
+    info.abi_version = lib.pkv_abi_version()
     info.kind = lib.PKV_KIND_DECODE
     info.page_size, info.num_kv_heads, info.head_dim, info.dtype = 16, 8, 128, 0
     kv = lib.pkv_paged_kv()
