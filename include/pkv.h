@@ -26,6 +26,12 @@
  *     call, except the workspace pointers a plan records (see pkv_plan_info).
  *   - `stream` is a hipStream_t passed as void* (NULL = default stream). Run
  *     and merge calls are asynchronous on that stream and do no host sync.
+ *   - Run, merge, single-decode (given its workspace) and append calls
+ *     launch a fixed sequence of kernels with no allocation, no memset and
+ *     no host synchronisation, so they may be captured into a HIP graph on
+ *     the stream and replayed: a replay reads whatever the captured buffers
+ *     hold at that time (the plan's workspaces must stay as they were). The
+ *     *_timed variants are excluded (their events belong to the caller).
  *   - Layouts are row-major and contiguous unless strides are given:
  *       q, o     : decode [batch, num_qo_heads, head_dim],
  *                  prefill [total_qo_tokens, num_qo_heads, head_dim];
