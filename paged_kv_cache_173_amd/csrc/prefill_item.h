@@ -143,18 +143,22 @@ __shared__ __attribute__((aligned(1024))) char sV1[kTileBytes];
 __shared__ __attribute__((aligned(1024))) char sV2[kTileBytes];
 __shared__ __attribute__((aligned(1024))) char sV3[kTileBytes];
 
-// RB = row blocks per wave: wave w owns rows 32*RB*w .. 32*RB*(w+1)-1 of an
-// item of 128*RB rows, in RB blocks of 32. Every K and V operand read from LDS
+// NW = waves per workgroup (4 or 8); RB = row blocks per wave: wave w owns
+// rows 32*RB*w .. 32*RB*(w+1)-1 of an item of 32*NW*RB rows, in RB blocks of
+// 32. The NW waves share every K / V tile (each stages KT/NW of its rows). Every K and V operand read from LDS
 // feeds RB MFMAs (one per block). The kernels use RB = 1 (two waves per SIMD,
 // 256 VGPRs). RB = 2 halves the LDS reads per MFMA but needs about 330
 // registers per lane, so one wave per SIMD; with the compiler placing the
 // score accumulators in AGPRs (every softmax touch then copies them out) it
 // gave bit-identical results 23 % slower on the causal prefill workload.
-template <class T, class OUT, int MODE, bool VAR, int RB = 1>
+template <class T, class OUT, int MODE, bool VAR, int RB = 1, int NW = 4>
 __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t* it) {
+  static_assert(NW == 4 || NW == 8, "a tile's 32 rows are staged in groups of four per load");
   using elem = typename T::elem;
   constexpr int D = kHeadDim;
-  constexpr int kRows = kTileRows * RB;    // query rows of one item
+  constexpr int kRows = 32 * NW * RB;     // query rows of one item
+  constexpr int kRpw = KT / NW;           // tile rows each wave stages
+  constexpr int kLpw = kRpw / 4;          // its loads per K or V tile (four rows each)
   auto kbuf = [&](auto ph) -> char* {
     constexpr int i = decltype(ph)::value & 3;
     if constexpr (i == 0) return sK0;
@@ -234,8 +238,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
       qv[rb][kk] = row_ok[rb] ? load_16B(qp + 16 * kk) : u32x4{0, 0, 0, 0};
   }
 
-  // ---- staging: wave w fetches token rows 8w .. 8w+7 of a tile; load j
-  // (0..1) covers rows 8w + 4j + lane/16, lane % 16 being the LDS chunk slot.
+  // ---- staging: wave w fetches token rows kRpw*w .. kRpw*(w+1)-1 of a tile;
+  // load j (0 .. kLpw-1) covers rows kRpw*w + 4j + lane/16, lane % 16 being
+  // the LDS chunk slot.
   const char* kbase = static_cast<const char*>(a.k) + static_cast<int64_t>(g) * a.head_stride * 2;
   const char* vbase = static_cast<const char*>(a.v) + static_cast<int64_t>(g) * a.head_stride * 2;
   const int P = a.page_size;
@@ -246,29 +251,31 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
   const __amdgpu_buffer_rsrc_t pt = make_rsrc(a.kv_indices + page0, 4u * static_cast<uint32_t>(npages));
   const int srow = lane >> 4, spos = lane & 15;
   // Global chunk fetched by this lane for load j (the inverse of the swizzle).
-  auto k_chunk = [&](int j) { return spos ^ (8 * (wave & 1) + 4 * j + srow); };
+  auto k_chunk = [&](int j) { return spos ^ ((kRpw * wave + 4 * j + srow) & 15); };
   const int v_chunk = spos ^ (4 * srow);
   auto lds_dst = [&](char* tile_base, int j) -> lds_void* {
-    return (lds_void*)(tile_base + (8 * wave + 4 * j) * kRowBytes);
+    return (lds_void*)(tile_base + (kRpw * wave + 4 * j) * kRowBytes);
   };
 
   // Page-uniform mode (page_size a power of two >= 16): page index (in the
-  // request) of the wave's 8-token group of tile ti. Item starts are page
+  // request) of the wave's kRpw-token group of tile ti. Item starts are page
   // aligned, so a group never straddles a page; the token is clamped into the
   // item, so the index is in range.
   const int pshift = __builtin_ctz(static_cast<unsigned>(P));
   auto group_page = [&](int ti) -> int {
-    const int tc = min(k0 + ti * KT + 8 * wave, k1 - 1);
+    const int tc = min(k0 + ti * KT + kRpw * wave, k1 - 1);
     return tc >> pshift;
   };
   // Generic mode: the lane's token for load j of tile ti (clamped likewise).
-  auto lane_token = [&](int ti, int j) -> int { return min(k0 + ti * KT + 8 * wave + 4 * j + srow, k1 - 1); };
+  auto lane_token = [&](int ti, int j) -> int {
+    return min(k0 + ti * KT + kRpw * wave + 4 * j + srow, k1 - 1);
+  };
 
   // Page ids of one tile's loads, fetched two iterations before they are
   // used: vector-memory loads complete in issue order, so a consumer of an id
   // waits for every load issued before it, and two iterations is when the
   // tile loads issued just before it are due anyway. Uniform mode: the group's
-  // id (wave-uniform); generic mode: the ids of the lane's two tokens. Loads
+  // id (wave-uniform); generic mode: the ids of the lane's kLpw tokens. Loads
   // past the page list read zero (the descriptor's range).
   struct Pids { int p[2]; };
   auto fetch_pids = [&](int ti) -> Pids {
@@ -278,7 +285,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
       r.p[1] = 0;
     } else {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < kLpw; ++j)
         r.p[j] = __builtin_amdgcn_raw_buffer_load_b32(pt, 4u * (lane_token(ti, j) / P), 0, 0);
     }
     return r;
@@ -288,18 +295,18 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
   // past the item read as zero). K and V of a tile share it.
   struct Group { uint64_t off; uint32_t nbytes; };
   auto group_of = [&](int ti, const Pids& pid) -> Group {
-    const int t = k0 + ti * KT + 8 * wave;
+    const int t = k0 + ti * KT + kRpw * wave;
     const uint32_t id = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(pid.p[0]));
     const uint32_t sl = static_cast<uint32_t>(min(t, k1 - 1) & (P - 1));
-    // clamp(k1 - t, 0, 8): wave-uniform (readfirstlane: the compiler forms the
-    // clamp with a vector med3)
-    const uint32_t nvalid = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(max(0, min(8, k1 - t))));
+    // clamp(k1 - t, 0, kRpw): wave-uniform (readfirstlane: the compiler forms
+    // the clamp with a vector med3)
+    const uint32_t nvalid = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(max(0, min(kRpw, k1 - t))));
     return {static_cast<uint64_t>(id) * ps_bytes + sl * ts_bytes, nvalid * ts_bytes};
   };
   auto issue_group = [&](const Group& gr, const char* base, char* dst, bool is_k) {
     const __amdgpu_buffer_rsrc_t r = make_rsrc(base + gr.off, gr.nbytes);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < kLpw; ++j) {
       const uint32_t row = static_cast<uint32_t>(4 * j + srow) * ts_bytes;
       buffer_to_lds_16B(r, lds_dst(dst, j), row + 16 * (is_k ? k_chunk(j) : v_chunk));
     }
@@ -310,7 +317,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
       issue_group(group_of(ti, pid), base, dst, is_k);
     } else {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < kLpw; ++j) {
         const int tc = lane_token(ti, j);
         const int sl = tc - (tc / P) * P;
         const uint64_t off = static_cast<uint64_t>(static_cast<uint32_t>(pid.p[j])) * ps_bytes + sl * ts_bytes;
@@ -583,7 +590,9 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
   // only in the iteration after the barrier that follows its last read.
   // Every iteration issues the same loads (tiles past the item read zero, or
   // repeat the last token in generic mode), so the wait counts are constants.
-  constexpr int kLoadsPerIter = MODE == kPagedUniform ? 5 : 6;
+  // Loads per iteration and wave: page ids (one uniform id, or one per lane
+  // token) and the kLpw loads of K and of V.
+  constexpr int kLoadsPerIter = MODE == kPagedUniform ? 1 + 2 * kLpw : 3 * kLpw;
   // Page ids of the K loads of tiles j+4 and j+5 and of the V load of tile j+3.
   Pids pid_k0, pid_k1, pid_v;
   Group grp_v{0, 0};   // uniform mode: where the V load of tile j+3 reads
