@@ -80,7 +80,7 @@ def profiled_traffic():
 
 
 # ----------------------------------------------------------------------------
-# algorithmic work (see the design doc for the per-unit figures)
+# algorithmic work per run: bytes that must cross HBM, flops of visible pairs
 # ----------------------------------------------------------------------------
 def decode_bytes(kv_lens, Hkv, D, elem, B, Hq):
     """K + V rows read once per (request, KV head), plus q, o and LSE."""
@@ -432,7 +432,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(the path would shard requests or KV chunks across GPUs, see DESIGN.md)",
+              f"(the path would shard requests, or one request's KV chunks, across GPUs)",
               file=sys.stderr)
         sys.exit(2)
 

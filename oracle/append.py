@@ -14,7 +14,7 @@ What is computed, and where the pages state it:
   kv_indices[kv_indptr[b] + t // P], slot t % P, NHD page memory
   [page, slot, kv_head, head_dim].
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings taken where the pages are silent:
 
 * Each appended row names its request b and its position t in that request.
 * The page table already describes the cache after the append, so the KV

@@ -31,7 +31,7 @@ What is computed, and where the FlashInfer pages state it:
   attention over the concatenated prefix + suffix tokens, which is what
   ``cascade_decode`` computes.
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings taken where the pages are silent:
 
 * The log-sum-exp is the natural log of sum exp(scale * q.k) over visible keys.
 * GQA: query head h reads KV head h // G with G = num_qo_heads // num_kv_heads.

@@ -14,7 +14,7 @@ What is computed, and where the pages state it:
   ``attention.py`` (article "FlashInfer", sections "Attention states" and
   "Extreme-negative-logit correction").
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings taken where the pages are silent:
 
 * The mask is a BSR matrix over blocks of R query tokens and C key tokens:
   query token i sees key t iff block t // C is listed for block row i // R;

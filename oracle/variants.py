@@ -14,7 +14,7 @@ What is computed, and where the pages state it:
   ``attention.py`` (article "FlashInfer", sections "Attention states",
   "Extreme-negative-logit correction", "Block-sparse cache representation").
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings taken where the pages are silent:
 
 * Sliding window, ``window_left`` = W (W < 0: no window). A query at absolute
   position p in its request's KV (prefill: p = i + L - Q for query token i of
