@@ -395,6 +395,124 @@ def cpu_baseline(w, min_s=10.0, max_s=30.0):
                       f"the {len(kv.kv_lens)} requests of the same batch, all heads) in {dt:.1f} s"}
 
 
+def oracle_units(runner):
+    """The oracle's work for one step of the runner's workload, cut into units (one request,
+    or one KV head for block-sparse attention), each with its share of the step's algorithmic
+    work (bytes for HBM-bound workloads, flops for MFMA-bound ones)."""
+    import oracle
+    w = runner.w
+    var = w.meta.get("variant", {}) if w.kind in ("decode", "prefill") else {}
+    win = int(var.get("window_left", -1))
+    cap = float(var.get("logits_soft_cap", 0.0))
+    sinks = var.get("sinks")
+    units = []
+    if w.kind == "single_decode":
+        units.append((lambda: oracle.single_decode(w.q, w.k, w.v, w.dtype, w.sm_scale), 1.0))
+    elif w.kind == "append":
+        kv = w.kv
+        bi, pos = oracle.append_positions(w.append_indptr, kv.kv_indptr, kv.last_page_len,
+                                          kv.page_size)
+        units.append((lambda: oracle.append_paged_kv(kv.k_cache, kv.v_cache, w.append_k,
+                                                     w.append_v, bi, pos, kv.kv_indptr,
+                                                     kv.kv_indices, kv.last_page_len), 1.0))
+    elif w.kind == "decode":
+        kv = w.kv
+        seen = kv.kv_lens if win < 0 else np.minimum(kv.kv_lens, win + 1)
+        total = float(np.sum(seen))
+        for b in range(len(seen)):
+            if win >= 0 or cap > 0 or sinks is not None:
+                fn = (lambda b=b: oracle.batch_decode_variant(
+                    w.q, kv.k_cache, kv.v_cache, kv.kv_indptr, kv.kv_indices, kv.last_page_len,
+                    w.dtype, w.sm_scale, win, cap, sinks, requests=[b]))
+            else:
+                fn = (lambda b=b: oracle.batch_decode(
+                    w.q, kv.k_cache, kv.v_cache, kv.kv_indptr, kv.kv_indices, kv.last_page_len,
+                    w.dtype, w.sm_scale, requests=[b]))
+            units.append((fn, float(seen[b]) / total if total else 0.0))
+    elif w.kind == "prefill":
+        kv = w.kv
+        qo = w.meta["qo_lens"]
+        fl = [prefill_flops([qo[b]], [kv.kv_lens[b]], w.num_qo_heads, w.head_dim, w.causal, win)
+              for b in range(len(qo))]
+        total = float(sum(fl))
+        for b in range(len(qo)):
+            if win >= 0 or cap > 0 or sinks is not None:
+                fn = (lambda b=b: oracle.batch_prefill_variant(
+                    w.q, kv.k_cache, kv.v_cache, w.qo_indptr, kv.kv_indptr, kv.kv_indices,
+                    kv.last_page_len, w.dtype, w.sm_scale, w.causal, win, cap, sinks,
+                    requests=[b]))
+            else:
+                fn = (lambda b=b: oracle.batch_prefill(
+                    w.q, kv.k_cache, kv.v_cache, w.qo_indptr, kv.kv_indptr, kv.kv_indices,
+                    kv.last_page_len, w.dtype, w.sm_scale, w.causal, requests=[b]))
+            units.append((fn, fl[b] / total if total else 0.0))
+    elif w.kind == "cascade":
+        kv = w.kv
+        B = len(kv.kv_lens)
+        for b in range(B):
+            units.append((lambda b=b: oracle.cascade_decode(
+                w.q, kv.k_cache, kv.v_cache, w.prefix_indices, w.prefix_last_page_len,
+                kv.kv_indptr, kv.kv_indices, kv.last_page_len, w.dtype, w.sm_scale,
+                requests=[b]), 1.0 / B))
+    elif w.kind == "block_sparse":
+        G = w.num_qo_heads // w.num_kv_heads
+        for g in range(w.num_kv_heads):
+            qs = np.ascontiguousarray(w.q[:, g * G:(g + 1) * G])
+            ks, vs = np.ascontiguousarray(w.k[:, g:g + 1]), np.ascontiguousarray(w.v[:, g:g + 1])
+            units.append((lambda qs=qs, ks=ks, vs=vs: oracle.block_sparse_attention(
+                qs, ks, vs, w.dtype, w.bsr_indptr, w.bsr_indices, w.row_block, w.col_block,
+                w.sm_scale), 1.0 / w.num_kv_heads))
+    elif w.kind == "pod":
+        wp, wd = w.prefill, w.decode
+        fp = [prefill_flops([wp.meta["qo_lens"][b]], [wp.kv.kv_lens[b]], wp.num_qo_heads,
+                            wp.head_dim, wp.causal) for b in range(len(wp.meta["qo_lens"]))]
+        fd = [4.0 * wd.num_qo_heads * wd.head_dim * float(L) for L in wd.kv.kv_lens]
+        total = float(sum(fp) + sum(fd))
+        for b in range(len(fp)):
+            units.append((lambda b=b: oracle.batch_prefill(
+                wp.q, wp.kv.k_cache, wp.kv.v_cache, wp.qo_indptr, wp.kv.kv_indptr,
+                wp.kv.kv_indices, wp.kv.last_page_len, wp.dtype, wp.sm_scale, wp.causal,
+                requests=[b]), fp[b] / total))
+        for b in range(len(fd)):
+            units.append((lambda b=b: oracle.batch_decode(
+                wd.q, wd.kv.k_cache, wd.kv.v_cache, wd.kv.kv_indptr, wd.kv.kv_indices,
+                wd.kv.last_page_len, wd.dtype, wd.sm_scale, requests=[b]), fd[b] / total))
+    return units
+
+
+def oracle_timing(runner, prefill_like, min_s=3.0, max_s=10.0):
+    """The oracle on the host cores over a bounded sample of one step's work (whole units in
+    order, at least `min_s` seconds, stopping after `max_s`), in the workload's roofline unit."""
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    nbytes, flops, _ = runner.work()
+    units = oracle_units(runner)
+    t0 = time.perf_counter()
+    share, n, passes = 0.0, 0, 0
+    while time.perf_counter() - t0 < min_s and units:
+        for fn, sh in units:
+            fn()
+            share += sh
+            n += 1
+            if time.perf_counter() - t0 > max_s:
+                break
+        passes += 1
+        if time.perf_counter() - t0 > max_s:
+            break
+    dt = time.perf_counter() - t0
+    work = (flops if prefill_like else nbytes) * share
+    return {"value": work / dt / (1e12 if prefill_like else 1e9),
+            "unit": "TFLOP/s" if prefill_like else "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 NumPy oracle, {n} unit evaluations ({len(units)} units make one "
+                      f"step; {share:.3f} steps' work) in {dt:.1f} s"}
+
+
+# workloads whose roofline is the MFMA peak (the rest are bound by HBM)
+PREFILL_LIKE = ("prefill", "block_sparse", "pod", "prefill_variants")
+
 WORKLOADS = {"single": 0, "decode": 1, "prefill": 2, "cascade": 3, "long": 4, "append": 5,
              "block_sparse": 6, "pod": 7, "decode_variants": 8, "prefill_variants": 9}
 
@@ -429,6 +547,8 @@ def main():
     ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
     ap.add_argument("--all", action="store_true", help="also measure the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baselines", action="store_true",
+                    help="also time the oracle on a bounded sample of every measured workload")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -477,6 +597,11 @@ def main():
             f"({100 * res['hbm_frac']:.1f}% HBM), {res['TFLOPs']:.1f} TFLOP/s; attention kernel "
             f"{kern_ms * 1e3:.1f} us: {res['kernel_GBps']:.0f} GB/s, "
             f"{res['kernel_TFLOPs']:.1f} TFLOP/s")
+        if args.cpu_baselines:
+            log(f"[bench] {name}: timing the CPU oracle on a bounded sample")
+            res["cpu_baseline"] = oracle_timing(r, name in PREFILL_LIKE)
+            log(f"[bench] {name}: oracle {res['cpu_baseline']['value']:.4g} "
+                f"{res['cpu_baseline']['unit']} ({res['cpu_baseline']['sample']})")
         results[name] = res
         if headline is None:
             headline = (name, w, r, res)
@@ -485,7 +610,7 @@ def main():
             torch.cuda.empty_cache()
 
     name, w, r, res = headline
-    prefill_like = name in ("prefill", "block_sparse", "pod", "prefill_variants")
+    prefill_like = name in PREFILL_LIKE
     line = {
         "metric": "paged decode HBM GB/s (% peak); prefill TFLOPS (% MFMA peak); tokens/s",
         "value": res["TFLOPs"] if prefill_like else res["GBps"],
