@@ -1,0 +1,58 @@
+"""Host-side checks of bench.py's oracle timing (no GPU): for every workload kind the
+oracle's units (requests, or KV heads for block-sparse attention) cover exactly one step's
+algorithmic work, and a bounded timing run gives a positive figure in the workload's unit."""
+
+import numpy as np
+import pytest
+
+import bench
+from paged_kv_cache_173_amd import workloads as wl
+
+
+class _Runner:
+    """The parts of bench.Runner that the work accounting reads."""
+
+    def __init__(self, w):
+        self.w = w
+        var = w.meta.get("variant", {}) if hasattr(w, "meta") else {}
+        self.window_left = int(var.get("window_left", -1))
+
+    def work(self):
+        return bench.Runner.work(self)
+
+
+CASES = {
+    "single": lambda: wl.single_decode(seed=1, kv_len=100, num_qo_heads=8, num_kv_heads=2),
+    "decode": lambda: wl.batch_decode(seed=2, batch=3, kv_min=0, kv_max=90, num_qo_heads=8,
+                                      num_kv_heads=2),
+    "decode_variants": lambda: bench.with_variants(
+        wl.batch_decode(seed=3, batch=3, kv_min=10, kv_max=90, num_qo_heads=8, num_kv_heads=2),
+        31, 30.0, 5),
+    "prefill": lambda: wl.batch_prefill(seed=4, batch=3, qo_min=0, qo_max=20, prefix_max=30,
+                                        num_qo_heads=8, num_kv_heads=2),
+    "prefill_variants": lambda: bench.with_variants(
+        wl.batch_prefill(seed=5, batch=2, qo_min=5, qo_max=20, prefix_max=30, num_qo_heads=8,
+                         num_kv_heads=2), 7, 50.0, 6),
+    "cascade": lambda: wl.cascade(seed=6, batch=3, prefix_len=40, suffix_lens=[3, 0, 17],
+                                  num_qo_heads=8, num_kv_heads=2),
+    "append": lambda: wl.append_kv(seed=7, batch=3, new_lens=[2, 0, 5], prefix_lens=[1, 3, 0],
+                                   num_kv_heads=2),
+    "block_sparse": lambda: wl.block_sparse(seed=8, num_qo_tokens=70, num_kv_tokens=90,
+                                            row_block=32, col_block=32, density=0.5,
+                                            num_qo_heads=4, num_kv_heads=2),
+    "pod": lambda: wl.pod(seed=9, p_batch=2, qo_min=3, qo_max=20, prefix_max=20, d_batch=3,
+                          kv_min=1, kv_max=50, num_qo_heads=8, num_kv_heads=2),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_oracle_units_cover_one_step(name):
+    r = _Runner(CASES[name]())
+    units = bench.oracle_units(r)
+    assert units, name
+    assert abs(sum(share for _, share in units) - 1.0) < 1e-9
+    assert all(share >= 0 for _, share in units)
+    res = bench.oracle_timing(r, name in bench.PREFILL_LIKE, min_s=1e-6, max_s=5.0)
+    assert res["value"] > 0 and np.isfinite(res["value"])
+    assert res["unit"] == ("TFLOP/s" if name in bench.PREFILL_LIKE else "GB/s")
+    assert res["kind"] == "oracle"
