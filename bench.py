@@ -482,7 +482,8 @@ def oracle_units(runner):
 
 def oracle_timing(runner, prefill_like, min_s=3.0, max_s=10.0):
     """The oracle on the host cores over a bounded sample of one step's work (whole units in
-    order, at least `min_s` seconds, stopping after `max_s`), in the workload's roofline unit."""
+    order: at least one pass and `min_s` seconds, stopping once past `max_s`), in the
+    workload's roofline unit."""
     try:
         from threadpoolctl import threadpool_info
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
@@ -491,16 +492,16 @@ def oracle_timing(runner, prefill_like, min_s=3.0, max_s=10.0):
     nbytes, flops, _ = runner.work()
     units = oracle_units(runner)
     t0 = time.perf_counter()
-    share, n, passes = 0.0, 0, 0
-    while time.perf_counter() - t0 < min_s and units:
+    share, n = 0.0, 0
+    while units:                      # at least one pass, then until min_s (or past max_s)
         for fn, sh in units:
             fn()
             share += sh
             n += 1
             if time.perf_counter() - t0 > max_s:
                 break
-        passes += 1
-        if time.perf_counter() - t0 > max_s:
+        elapsed = time.perf_counter() - t0
+        if elapsed >= min_s or elapsed > max_s:
             break
     dt = time.perf_counter() - t0
     work = (flops if prefill_like else nbytes) * share

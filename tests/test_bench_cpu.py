@@ -52,7 +52,7 @@ def test_oracle_units_cover_one_step(name):
     assert units, name
     assert abs(sum(share for _, share in units) - 1.0) < 1e-9
     assert all(share >= 0 for _, share in units)
-    res = bench.oracle_timing(r, name in bench.PREFILL_LIKE, min_s=1e-6, max_s=5.0)
+    res = bench.oracle_timing(r, name in bench.PREFILL_LIKE, min_s=0.0, max_s=5.0)
     assert res["value"] > 0 and np.isfinite(res["value"])
     assert res["unit"] == ("TFLOP/s" if name in bench.PREFILL_LIKE else "GB/s")
     assert res["kind"] == "oracle"
