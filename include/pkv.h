@@ -242,6 +242,35 @@ pkv_status pkv_plan_host(pkv_kind kind, const int32_t* qo_indptr_h, const int32_
                          int32_t items_cap,
                          int32_t* groups_out, int32_t groups_cap, int32_t* counts_out);
 
+/* Workspace sizes (bytes) that suffice for every plan of `kind` with at most
+ * `max_items` work items (for the cascade and the mixed batch: both parts
+ * together), whatever the lengths, so a caller can allocate once before
+ * planning (graph capture, serving loops). `batch`: requests (decode,
+ * prefill), query blocks (block-sparse), suffix requests (cascade), prefill
+ * plus decode requests (mixed batch). Sizes follow the plan calls' own
+ * layout with max_items items, merge groups and partial-state slots (a plan
+ * never has more groups or slots than items), so they are upper bounds; a
+ * plan that splits fewer items needs less float workspace. The exact item
+ * count of given lengths is counts_out[0] of pkv_plan_host. No GPU call.
+ * Errors: INVALID_ARG (NULL outputs, negative sizes, heads not a multiple,
+ * unknown kind), UNSUPPORTED (head_dim != 128, G above the kind's limit). */
+pkv_status pkv_workspace_size(pkv_kind kind, int32_t batch, int32_t num_qo_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int64_t max_items,
+                              size_t* int_ws_bytes, size_t* float_ws_bytes,
+                              size_t* host_ws_bytes);
+
+/* Copies part `part` (0; or 1, the decode part, for a cascade or mixed-batch
+ * plan) of a plan's work list to the caller: items_out[num_items][8] and
+ * groups_out[num_groups][8] in the layout of pkv_plan_host (counts in
+ * plan->part[part]). Reads the host workspace the plan was made with, which
+ * must not have been reused since. No GPU call. Errors: PLAN_MISMATCH (not a
+ * plan of this library version), INVALID_ARG (part out of range, NULL
+ * buffers where rows exist), WORKSPACE_TOO_SMALL (items_cap / groups_cap
+ * below the counts; nothing is written). */
+pkv_status pkv_plan_export(const pkv_plan_info* plan, const void* host_ws, int32_t part,
+                           int32_t* items_out, int32_t items_cap, int32_t* groups_out,
+                           int32_t groups_cap);
+
 /* ---------------------------------------------------------------------------
  * Batch paged decode: one query token per request.
  *

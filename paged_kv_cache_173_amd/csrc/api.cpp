@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <limits>
 #include <string>
 #include <vector>
 
@@ -197,28 +198,37 @@ struct Layout {
   int64_t float_bytes = 0;
 };
 
-// Places one part's tables and partial states at the current end of each workspace.
-void place_part(const pkv::HostPlan& hp, int64_t batch, int32_t rows_per_tile, int32_t causal,
-                Layout* lay, pkv_plan_part* part, int32_t window_left = -1) {
-  part->num_items = static_cast<int32_t>(hp.items.size());
-  part->num_groups = static_cast<int32_t>(hp.groups.size());
-  part->chunk_pages = hp.chunk_pages;
+// Places one part's tables (items, merge groups: 8 int32 each; KV lengths:
+// batch int32) and partial states (num_slots slots of rows_per_tile rows) at
+// the current end of each workspace.
+void place_counts(int64_t num_items, int64_t num_groups, int64_t num_slots, int32_t chunk_pages,
+                  int64_t batch, int32_t rows_per_tile, int32_t causal, Layout* lay,
+                  pkv_plan_part* part, int32_t window_left = -1) {
+  part->num_items = static_cast<int32_t>(num_items);
+  part->num_groups = static_cast<int32_t>(num_groups);
+  part->chunk_pages = chunk_pages;
   part->rows_per_tile = rows_per_tile;
-  part->num_slots = hp.num_slots;
+  part->num_slots = static_cast<int32_t>(num_slots);
   part->causal = causal;
   part->window_left = window_left;
   part->items_off = lay->int_bytes;
-  lay->int_bytes = align_up(lay->int_bytes + static_cast<int64_t>(hp.items.size()) * 32);
+  lay->int_bytes = align_up(lay->int_bytes + num_items * 32);
   part->groups_off = lay->int_bytes;
-  lay->int_bytes = align_up(lay->int_bytes + static_cast<int64_t>(hp.groups.size()) * 32);
+  lay->int_bytes = align_up(lay->int_bytes + num_groups * 32);
   part->kv_len_off = lay->int_bytes;
   lay->int_bytes = align_up(lay->int_bytes + batch * 4);
   part->part_o_off = lay->float_bytes;
-  lay->float_bytes = align_up(lay->float_bytes + static_cast<int64_t>(hp.num_slots) *
-                                                     rows_per_tile * pkv::kHeadDimSupported * 4);
-  part->part_lse_off = lay->float_bytes;
   lay->float_bytes =
-      align_up(lay->float_bytes + static_cast<int64_t>(hp.num_slots) * rows_per_tile * 4);
+      align_up(lay->float_bytes + num_slots * rows_per_tile * pkv::kHeadDimSupported * 4);
+  part->part_lse_off = lay->float_bytes;
+  lay->float_bytes = align_up(lay->float_bytes + num_slots * rows_per_tile * 4);
+}
+
+void place_part(const pkv::HostPlan& hp, int64_t batch, int32_t rows_per_tile, int32_t causal,
+                Layout* lay, pkv_plan_part* part, int32_t window_left = -1) {
+  place_counts(static_cast<int64_t>(hp.items.size()), static_cast<int64_t>(hp.groups.size()),
+               hp.num_slots, hp.chunk_pages, batch, rows_per_tile, causal, lay, part,
+               window_left);
 }
 
 void write_part(const pkv::HostPlan& hp, const std::vector<int64_t>& kv_lens,
@@ -467,6 +477,91 @@ pkv_status pkv_default_sched_for(pkv_kind kind, int32_t device, pkv_sched* out) 
   // the end on the 64-request and 4 x 128k-token workloads). Prefill: one wave;
   // its tiles already give several items per workgroup.
   if (occ > 0) out->wg_per_cu = kind == PKV_KIND_DECODE ? (5 * occ + 1) / 2 : occ;
+  return ok();
+}
+
+pkv_status pkv_workspace_size(pkv_kind kind, int32_t batch, int32_t num_qo_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int64_t max_items,
+                              size_t* int_ws_bytes, size_t* float_ws_bytes,
+                              size_t* host_ws_bytes) {
+  if (int_ws_bytes == nullptr || float_ws_bytes == nullptr || host_ws_bytes == nullptr)
+    return fail(PKV_ERR_INVALID_ARG, "output pointers must be non-NULL");
+  if (batch < 0 || max_items < 0) return fail(PKV_ERR_INVALID_ARG, "batch and max_items must be >= 0");
+  if (num_qo_heads <= 0 || num_kv_heads <= 0 || num_qo_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_qo_heads must be a positive multiple of num_kv_heads");
+  if (head_dim != pkv::kHeadDimSupported)
+    return fail(PKV_ERR_UNSUPPORTED, "only head_dim 128 is implemented");
+  if (max_items > std::numeric_limits<int32_t>::max())
+    return fail(PKV_ERR_INVALID_ARG, "max_items overflows int32");
+  const int32_t G = num_qo_heads / num_kv_heads;
+  // A plan of any lengths with at most max_items items: its merge groups and
+  // partial-state slots are never more than its items, so max_items of each,
+  // placed the way the kind's plan call places its parts, bounds every table.
+  // Two-part kinds give each part the whole bound.
+  const int64_t n = max_items;
+  Layout lay;
+  pkv_plan_part part[2]{};
+  switch (kind) {
+    case PKV_KIND_DECODE:
+      if (G > kMaxDecodeGroup) return fail(PKV_ERR_UNSUPPORTED, "decode supports G <= 16");
+      place_counts(n, n, n, 0, batch, G, 0, &lay, &part[0]);
+      break;
+    case PKV_KIND_PREFILL:
+      if (G > kRowsPerPrefillTile) return fail(PKV_ERR_UNSUPPORTED, "prefill supports G <= 128");
+      place_counts(n, n, n, 0, batch, kRowsPerPrefillTile, 0, &lay, &part[0]);
+      break;
+    case PKV_KIND_BLOCK_SPARSE:   // batch = query blocks
+      if (G > kRowsPerPrefillTile) return fail(PKV_ERR_UNSUPPORTED, "prefill supports G <= 128");
+      lay.int_bytes = align_up((static_cast<int64_t>(batch) + 1) * 4);
+      place_counts(n, n, n, 0, batch, kRowsPerPrefillTile, 0, &lay, &part[0]);
+      break;
+    case PKV_KIND_CASCADE: {      // batch = requests (suffixes)
+      if (G > kMaxDecodeGroup) return fail(PKV_ERR_UNSUPPORTED, "cascade supports G <= 16");
+      lay.int_bytes = kAlign;
+      place_counts(n, n, n, 0, 1, kRowsPerPrefillTile, 0, &lay, &part[0]);
+      place_counts(n, n, n, 0, batch, G, 0, &lay, &part[1]);
+      const int64_t rows = static_cast<int64_t>(batch) * num_qo_heads;
+      lay.float_bytes += 2 * (align_up(rows * head_dim * 4) + align_up(rows * 4));
+      break;
+    }
+    case PKV_KIND_POD:            // batch = prefill requests + decode requests
+      if (G > kMaxDecodeGroup) return fail(PKV_ERR_UNSUPPORTED, "the mixed launch supports G <= 16");
+      place_counts(n, n, n, 0, batch, kRowsPerPodPrefillTile, 0, &lay, &part[0]);
+      place_counts(n, n, n, 0, batch, G, 0, &lay, &part[1]);
+      lay.int_bytes = align_up(lay.int_bytes + n * 4);
+      break;
+    default:
+      return fail(PKV_ERR_INVALID_ARG, "unknown plan kind");
+  }
+  *int_ws_bytes = static_cast<size_t>(lay.int_bytes);
+  *float_ws_bytes = static_cast<size_t>(lay.float_bytes);
+  *host_ws_bytes = static_cast<size_t>(lay.int_bytes);
+  return ok();
+}
+
+pkv_status pkv_plan_export(const pkv_plan_info* plan, const void* host_ws, int32_t part,
+                           int32_t* items_out, int32_t items_cap, int32_t* groups_out,
+                           int32_t groups_cap) {
+  if (plan == nullptr) return fail(PKV_ERR_INVALID_ARG, "plan is NULL");
+  if (plan->magic != kPlanMagic || plan->abi_version != PKV_ABI_VERSION)
+    return fail(PKV_ERR_PLAN_MISMATCH, "not a plan made by this library version");
+  const bool two_parts = plan->kind == PKV_KIND_CASCADE || plan->kind == PKV_KIND_POD;
+  if (part < 0 || part > (two_parts ? 1 : 0))
+    return fail(PKV_ERR_INVALID_ARG, "part must be 0 (or 1 for a cascade or mixed-batch plan)");
+  const pkv_plan_part& pp = plan->part[part];
+  if (items_cap < pp.num_items || groups_cap < pp.num_groups)
+    return fail(PKV_ERR_WORKSPACE_TOO_SMALL,
+                "need room for " + std::to_string(pp.num_items) + " items and " +
+                    std::to_string(pp.num_groups) + " groups");
+  if ((pp.num_items > 0 || pp.num_groups > 0) && host_ws == nullptr)
+    return fail(PKV_ERR_INVALID_ARG, "host_ws is NULL");
+  if ((pp.num_items > 0 && items_out == nullptr) || (pp.num_groups > 0 && groups_out == nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "output arrays must be non-NULL when the part has rows");
+  const char* h = static_cast<const char*>(host_ws);
+  if (pp.num_items > 0)
+    std::memcpy(items_out, h + pp.items_off, static_cast<size_t>(pp.num_items) * 32);
+  if (pp.num_groups > 0)
+    std::memcpy(groups_out, h + pp.groups_off, static_cast<size_t>(pp.num_groups) * 32);
   return ok();
 }
 

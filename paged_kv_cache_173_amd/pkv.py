@@ -92,6 +92,11 @@ _VARP = ctypes.POINTER(pkv_variant)
 _lib_plan_host = _sig("pkv_plan_host", _I32,
                       [_I32, _I32P, _I32P, _I32P, _I32, _I32, _I32, _I32, _I32, _I32,
                        ctypes.POINTER(pkv_sched), _I32P, _I32, _I32P, _I32, _I32P])
+_lib_workspace_size = _sig("pkv_workspace_size", _I32,
+                           [_I32, _I32, _I32, _I32, _I32, _I64, ctypes.POINTER(_SZ),
+                            ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)])
+_lib_plan_export = _sig("pkv_plan_export", _I32,
+                        [ctypes.POINTER(pkv_plan_info), _P, _I32, _I32P, _I32, _I32P, _I32])
 _lib_decode_plan = _sig("pkv_decode_plan", _I32,
                         [_I32P, _I32P, _I32, _I32, _I32, _I32, _I32, _I32, _VARP,
                          ctypes.POINTER(pkv_sched), _P, _SZ, _P, _SZ, _P, _SZ, _P,
@@ -629,6 +634,27 @@ def pkv_append_positions(append_indptr, kv_indptr, last_page_len, page_size):
     _check(_lib_append_positions(_i32p(aip), _i32p(kip), _i32p(lpl), len(kip) - 1, int(page_size),
                                  _i32p(bi), _i32p(pos)), "pkv_append_positions")
     return bi[:nnz], pos[:nnz]
+
+
+def pkv_workspace_size(kind, batch, num_qo_heads, num_kv_heads, head_dim, max_items):
+    """(int_ws_bytes, float_ws_bytes, host_ws_bytes) enough for any plan of `kind` with at
+    most `max_items` work items."""
+    i, f, h = _SZ(0), _SZ(0), _SZ(0)
+    _check(_lib_workspace_size(int(kind), int(batch), int(num_qo_heads), int(num_kv_heads),
+                               int(head_dim), int(max_items), ctypes.byref(i), ctypes.byref(f),
+                               ctypes.byref(h)), "pkv_workspace_size")
+    return int(i.value), int(f.value), int(h.value)
+
+
+def pkv_plan_export(plan: pkv_plan_info, workspace: Workspace, part: int = 0):
+    """A part's (items [n, 8], groups [m, 8]) from the host workspace the plan was made with."""
+    p = plan.part[part] if 0 <= part < 2 else plan.part[0]
+    items = np.zeros((max(1, p.num_items), 8), dtype=np.int32)
+    groups = np.zeros((max(1, p.num_groups), 8), dtype=np.int32)
+    _check(_lib_plan_export(ctypes.byref(plan), workspace.host_ws.data_ptr(), int(part),
+                            _i32p(items), int(p.num_items), _i32p(groups), int(p.num_groups)),
+           "pkv_plan_export")
+    return items[:p.num_items].copy(), groups[:p.num_groups].copy()
 
 
 def read_plan_tables(plan: pkv_plan_info, workspace: Workspace, part: int = 0):
