@@ -36,8 +36,12 @@
  *       q, o     : decode [batch, num_qo_heads, head_dim],
  *                  prefill [total_qo_tokens, num_qo_heads, head_dim];
  *       lse      : float32, natural log, [rows, num_qo_heads];
- *       KV pages : NHD, element (page, slot, kv_head, d) at
- *                  base + page*page_stride + slot*token_stride + kv_head*head_stride + d.
+ *       KV pages : element (page, slot, kv_head, d) at
+ *                  base + page*page_stride + slot*token_stride + kv_head*head_stride + d,
+ *                  so both page layouts of the docs index ("Layout: NHD/HND") are
+ *                  described by strides: NHD token_stride = Hkv*head_dim,
+ *                  head_stride = head_dim; HND token_stride = head_dim,
+ *                  head_stride = page_size*head_dim.
  *   - Page tables are int32: kv_indptr[batch+1] (monotone), kv_indices[...]
  *     (page ids), last_page_len[batch] (1..page_size for a request with
  *     pages, 0 for a request with none). Request b holds

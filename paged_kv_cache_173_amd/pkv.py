@@ -219,8 +219,9 @@ def _device_tensor(t: torch.Tensor, name: str) -> torch.Tensor:
 
 
 def paged_kv(k_cache: torch.Tensor, v_cache: torch.Tensor) -> pkv_paged_kv:
-    """Describe NHD page pools k_cache / v_cache [num_pages, P, Hkv, D] (any strides
-    with a contiguous last dimension)."""
+    """Describe page pools k_cache / v_cache indexed [num_pages, P, Hkv, D] (any strides
+    with a contiguous last dimension): an NHD pool as it is, an HND pool (stored
+    [num_pages, Hkv, P, D]) as its view .permute(0, 2, 1, 3)."""
     if k_cache.shape != v_cache.shape or k_cache.stride() != v_cache.stride():
         raise ValueError("k_cache and v_cache must have the same shape and strides")
     if k_cache.dim() != 4 or k_cache.stride(3) != 1:
