@@ -280,9 +280,15 @@ pkv_status pkv_plan_export(const pkv_plan_info* plan, const void* host_ws, int32
  *
  * plan: validates the host page-table copies, applies the rule above, writes
  * the item and group tables into host_ws (pinned memory recommended) and
- * copies them to int_ws on `stream`, then waits for that copy (so host_ws is
- * reusable on return). With int_ws / float_ws NULL or too small it returns
- * WORKSPACE_TOO_SMALL and reports the required sizes in *out.
+ * queues one copy of them to int_ws on `stream`, without waiting for it: work
+ * queued later on `stream` (the run) sees the tables; work on another stream
+ * must be ordered after `stream` first. host_ws must stay allocated and
+ * unmodified until that copy has completed. A later plan call (of any kind)
+ * given the same host_ws waits for it before writing there, so one staging
+ * buffer can serve every plan call; the wait covers only that copy and what
+ * was queued on its stream before it. With int_ws / float_ws NULL or too small
+ * it returns WORKSPACE_TOO_SMALL, queues nothing and reports the required
+ * sizes in *out.
  * run: checks that the plan matches `kv` and launches the decode kernel and,
  * if any group split, the merge kernel. q [batch, Hq, 128], o like q
  * (same dtype as the cache), lse [batch, Hq] float32 or NULL.

@@ -9,7 +9,9 @@
 #include <algorithm>
 #include <cstring>
 #include <limits>
+#include <mutex>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "kernels.h"
@@ -242,8 +244,63 @@ void write_part(const pkv::HostPlan& hp, const std::vector<int64_t>& kv_lens,
                 hp.groups.size() * sizeof(pkv::MergeGroup));
 }
 
-// Checks the workspaces, then copies host_ws[0:int_bytes] to int_ws on the
-// stream and waits for the copy.
+// The last plan copy out of each host staging buffer: an event recorded on the
+// copy's stream right after it. A plan call waits for that event before it
+// writes the same buffer again, so one staging buffer serves every plan call
+// without the plan waiting for its own copy (or for the work queued before it).
+struct StagingCopy {
+  hipEvent_t done = nullptr;
+  hipDevice_t device = -1;
+};
+std::mutex g_staging_mu;
+std::unordered_map<const void*, StagingCopy> g_staging;
+
+// Sets *h to host_ws once no earlier plan copy still reads it, or to NULL when
+// host_ws is NULL or smaller than `need` (nothing is written then).
+pkv_status claim_staging(void* host_ws, size_t host_ws_bytes, int64_t need, char** h) {
+  *h = nullptr;
+  if (host_ws == nullptr || host_ws_bytes < static_cast<size_t>(need)) return PKV_OK;
+  std::lock_guard<std::mutex> lock(g_staging_mu);
+  auto it = g_staging.find(host_ws);
+  if (it != g_staging.end()) {
+    const hipError_t e = hipEventSynchronize(it->second.done);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(plan staging copy)");
+  }
+  *h = static_cast<char*>(host_ws);
+  return PKV_OK;
+}
+
+// Records the completion of a copy out of host_ws queued on `stream`.
+pkv_status record_staging(const void* host_ws, hipStream_t stream) {
+  hipDevice_t dev = 0;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+  std::lock_guard<std::mutex> lock(g_staging_mu);
+  StagingCopy& c = g_staging[host_ws];
+  if (c.done != nullptr && c.device != dev) {
+    (void)hipEventDestroy(c.done);
+    c.done = nullptr;
+  }
+  if (c.done == nullptr) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+    e = hipEventCreateWithFlags(&c.done, hipEventDisableTiming);
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess) {
+      c.done = nullptr;
+      g_staging.erase(host_ws);
+      return hip_fail(e, "hipEventCreateWithFlags(plan staging copy)");
+    }
+    c.device = dev;
+  }
+  if ((e = hipEventRecord(c.done, stream)) != hipSuccess)
+    return hip_fail(e, "hipEventRecord(plan staging copy)");
+  return PKV_OK;
+}
+
+// Checks the workspaces, then queues the copy of host_ws[0:int_bytes] to
+// int_ws on the stream and records its completion for host_ws.
 pkv_status commit_plan(const Layout& lay, void* int_ws, size_t int_ws_bytes, void* float_ws,
                        size_t float_ws_bytes, void* host_ws, size_t host_ws_bytes,
                        hipStream_t stream, pkv_plan_info* out) {
@@ -265,8 +322,8 @@ pkv_status commit_plan(const Layout& lay, void* int_ws, size_t int_ws_bytes, voi
   if (lay.int_bytes > 0) {
     hipError_t e = hipMemcpyAsync(int_ws, host_ws, lay.int_bytes, hipMemcpyHostToDevice, stream);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan)");
-    e = hipStreamSynchronize(stream);
-    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize(plan)");
+    pkv_status st = record_staging(host_ws, stream);
+    if (st) return st;
   }
   return PKV_OK;
 }
@@ -647,8 +704,9 @@ pkv_status pkv_decode_plan(const int32_t* kv_indptr_h, const int32_t* last_page_
               batch, s);
   Layout lay;
   place_part(hp, batch, G, 0, &lay, &out->part[0], window_left);
-  if (host_ws != nullptr && host_ws_bytes >= static_cast<size_t>(lay.int_bytes))
-    write_part(hp, kv_lens, out->part[0], static_cast<char*>(host_ws));
+  char* h = nullptr;
+  if ((st = claim_staging(host_ws, host_ws_bytes, lay.int_bytes, &h))) return st;
+  if (h != nullptr) write_part(hp, kv_lens, out->part[0], h);
   if ((st = commit_plan(lay, int_ws, int_ws_bytes, float_ws, float_ws_bytes, host_ws,
                         host_ws_bytes, static_cast<hipStream_t>(stream), out)))
     return st;
@@ -720,8 +778,9 @@ pkv_status pkv_prefill_plan(const int32_t* qo_indptr_h, const int32_t* kv_indptr
               page_size, static_cast<int32_t>(total_qo), s);
   Layout lay;
   place_part(hp, batch, kRowsPerPrefillTile, causal, &lay, &out->part[0], window_left);
-  if (host_ws != nullptr && host_ws_bytes >= static_cast<size_t>(lay.int_bytes))
-    write_part(hp, kv_lens, out->part[0], static_cast<char*>(host_ws));
+  char* h = nullptr;
+  if ((st = claim_staging(host_ws, host_ws_bytes, lay.int_bytes, &h))) return st;
+  if (h != nullptr) write_part(hp, kv_lens, out->part[0], h);
   if ((st = commit_plan(lay, int_ws, int_ws_bytes, float_ws, float_ws_bytes, host_ws,
                         host_ws_bytes, static_cast<hipStream_t>(stream), out)))
     return st;
@@ -938,8 +997,9 @@ pkv_status pkv_cascade_plan(int32_t prefix_num_pages, int32_t prefix_last_page_l
   out->cascade_state_off = lay.float_bytes;
   const int64_t rows = static_cast<int64_t>(batch) * num_qo_heads;
   lay.float_bytes += 2 * (align_up(rows * head_dim * 4) + align_up(rows * 4));
-  if (host_ws != nullptr && host_ws_bytes >= static_cast<size_t>(lay.int_bytes)) {
-    char* h = static_cast<char*>(host_ws);
+  char* h = nullptr;
+  if ((st = claim_staging(host_ws, host_ws_bytes, lay.int_bytes, &h))) return st;
+  if (h != nullptr) {
     const int32_t hdr[4] = {0, batch, 0, prefix_num_pages};
     std::memcpy(h, hdr, sizeof(hdr));
     write_part(hp0, pre_len, out->part[0], h);
@@ -1036,8 +1096,9 @@ pkv_status pkv_pod_plan(const int32_t* qo_indptr_h, const int32_t* kv_indptr_p_h
   place_part(hd, batch_d, G, 0, &lay, &out->part[1]);
   out->order_off = lay.int_bytes;
   lay.int_bytes = align_up(lay.int_bytes + static_cast<int64_t>(order.size()) * 4);
-  if (host_ws != nullptr && host_ws_bytes >= static_cast<size_t>(lay.int_bytes)) {
-    char* h = static_cast<char*>(host_ws);
+  char* h = nullptr;
+  if ((st = claim_staging(host_ws, host_ws_bytes, lay.int_bytes, &h))) return st;
+  if (h != nullptr) {
     write_part(hp, kv_p, out->part[0], h);
     write_part(hd, kv_d, out->part[1], h);
     if (!order.empty()) std::memcpy(h + out->order_off, order.data(), order.size() * 4);
@@ -1161,12 +1222,14 @@ pkv_status pkv_block_sparse_plan(const int32_t* bsr_indptr_h, const int32_t* bsr
   // int ws: the query-block offsets [num_block_rows + 1], then the part's tables
   lay.int_bytes = align_up((static_cast<int64_t>(num_block_rows) + 1) * 4);
   place_part(hp, num_block_rows, kRowsPerPrefillTile, 0, &lay, &out->part[0]);
-  if (host_ws != nullptr && host_ws_bytes >= static_cast<size_t>(lay.int_bytes)) {
-    int32_t* qo = static_cast<int32_t*>(host_ws);
+  char* h = nullptr;
+  if ((st = claim_staging(host_ws, host_ws_bytes, lay.int_bytes, &h))) return st;
+  if (h != nullptr) {
+    int32_t* qo = reinterpret_cast<int32_t*>(h);
     for (int32_t i = 0; i <= num_block_rows; ++i)
       qo[i] = static_cast<int32_t>(std::min<int64_t>(static_cast<int64_t>(i) * row_block,
                                                      num_qo_tokens));
-    write_part(hp, kv_lens, out->part[0], static_cast<char*>(host_ws));
+    write_part(hp, kv_lens, out->part[0], h);
   }
   if ((st = commit_plan(lay, int_ws, int_ws_bytes, float_ws, float_ws_bytes, host_ws,
                         host_ws_bytes, static_cast<hipStream_t>(stream), out)))

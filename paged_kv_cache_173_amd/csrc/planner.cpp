@@ -15,12 +15,6 @@ struct TileExtent {
   int64_t kv_end, page_lo, pages;
 };
 
-struct Keyed {
-  int64_t tokens;
-  int32_t b, tile, g, j;
-  PlanItem item;
-};
-
 }  // namespace
 
 bool build_plan(const PlanInput& in, HostPlan* out, std::string* err) {
@@ -32,6 +26,7 @@ bool build_plan(const PlanInput& in, HostPlan* out, std::string* err) {
   // after the last row's causal limit and, with a sliding window, starts at
   // the first row's window start (rounded down to a page).
   std::vector<TileExtent> tiles;
+  tiles.reserve(static_cast<size_t>(std::max(in.batch, 0)));
   int64_t page_sum = 0;
   for (int32_t b = 0; b < in.batch; ++b) {
     const int64_t Q = in.qo_lens[b], L = in.kv_lens[b];
@@ -64,8 +59,20 @@ bool build_plan(const PlanInput& in, HostPlan* out, std::string* err) {
     return false;
   }
 
-  std::vector<Keyed> keyed;
+  // Items in (b, tile, g, j) order, with their token counts. Slots are at
+  // most the items, so both counts fit int32 once the items do.
+  int64_t n_items = 0;
+  for (const TileExtent& te : tiles)
+    n_items += std::max<int64_t>(1, ceil_div(te.pages, c)) * in.num_kv_heads;
+  if (n_items > std::numeric_limits<int32_t>::max()) {
+    *err = "item count overflows int32";
+    return false;
+  }
+  std::vector<PlanItem> gen(static_cast<size_t>(n_items));
+  std::vector<uint32_t> tokens(static_cast<size_t>(n_items));
+  size_t n = 0;
   int64_t slot = 0;
+  uint32_t max_tokens = 0;
   for (const TileExtent& te : tiles) {
     const int64_t n_chunks = std::max<int64_t>(1, ceil_div(te.pages, c));
     for (int32_t g = 0; g < in.num_kv_heads; ++g) {
@@ -82,7 +89,7 @@ bool build_plan(const PlanInput& in, HostPlan* out, std::string* err) {
         slot += n_chunks;
       }
       for (int64_t j = 0; j < n_chunks; ++j) {
-        PlanItem it{};
+        PlanItem& it = gen[n];
         it.b = te.b;
         it.g = g;
         it.tile = te.tile;
@@ -93,26 +100,33 @@ bool build_plan(const PlanInput& in, HostPlan* out, std::string* err) {
         it.kv_begin = static_cast<int32_t>(k0);
         it.kv_end = static_cast<int32_t>(k1);
         it.slot = n_chunks > 1 ? static_cast<int32_t>(slot_begin + j) : -1;
-        keyed.push_back({k1 - k0, te.b, te.tile, g, static_cast<int32_t>(j), it});
+        tokens[n] = static_cast<uint32_t>(k1 - k0);
+        max_tokens = std::max(max_tokens, tokens[n]);
+        ++n;
       }
     }
   }
-  if (slot > std::numeric_limits<int32_t>::max() ||
-      keyed.size() > static_cast<size_t>(std::numeric_limits<int32_t>::max())) {
-    *err = "item or slot count overflows int32";
-    return false;
+  // Longest first; ties keep the (b, tile, g, j) order above. The key
+  // max_tokens - tokens is sorted ascending by a stable least-significant-digit
+  // radix sort over 11-bit digits (one pass while every item is shorter than
+  // 2048 tokens, at most three).
+  constexpr int kDigitBits = 11;
+  constexpr uint32_t kDigits = 1u << kDigitBits;
+  std::vector<uint32_t> order(n), next(n);
+  for (size_t i = 0; i < n; ++i) order[i] = static_cast<uint32_t>(i);
+  std::vector<uint32_t> count(kDigits + 1);
+  for (int shift = 0; shift < 32 && (max_tokens >> shift) != 0; shift += kDigitBits) {
+    std::fill(count.begin(), count.end(), 0u);
+    for (size_t i = 0; i < n; ++i) ++count[((max_tokens - tokens[i]) >> shift) % kDigits + 1];
+    for (uint32_t d = 0; d < kDigits; ++d) count[d + 1] += count[d];
+    for (size_t i = 0; i < n; ++i) {
+      const uint32_t k = order[i];
+      next[count[((max_tokens - tokens[k]) >> shift) % kDigits]++] = k;
+    }
+    order.swap(next);
   }
-
-  // Longest first; ties in (b, tile, g, j) order.
-  std::sort(keyed.begin(), keyed.end(), [](const Keyed& x, const Keyed& y) {
-    if (x.tokens != y.tokens) return x.tokens > y.tokens;
-    if (x.b != y.b) return x.b < y.b;
-    if (x.tile != y.tile) return x.tile < y.tile;
-    if (x.g != y.g) return x.g < y.g;
-    return x.j < y.j;
-  });
-  out->items.reserve(keyed.size());
-  for (const Keyed& k : keyed) out->items.push_back(k.item);
+  out->items.resize(n);
+  for (size_t i = 0; i < n; ++i) out->items[i] = gen[order[i]];
   out->chunk_pages = static_cast<int32_t>(c);
   out->num_slots = static_cast<int32_t>(slot);
   return true;

@@ -240,7 +240,9 @@ class Workspace:
     """Device int / float workspaces plus a pinned host staging buffer for plans.
 
     A plan records the workspace addresses; keep this object alive (and do not
-    grow it) for as long as the plan is used.
+    grow it) for as long as the plan is used. A plan call queues the copy of its
+    tables out of host_ws on its stream without waiting; the library makes the
+    next plan call on this workspace wait for that copy before it writes host_ws.
     """
 
     def __init__(self, int_bytes: int = 8 << 20, float_bytes: int = 64 << 20, device=None):
@@ -254,6 +256,8 @@ class Workspace:
                 self.float_ws.numel(), self.host_ws.data_ptr(), self.host_ws.numel())
 
     def grow(self, int_bytes: int, float_bytes: int) -> None:
+        # earlier plans' copies may still read host_ws and write int_ws
+        torch.cuda.synchronize(self.device)
         if int_bytes > self.int_ws.numel():
             self.int_ws = torch.empty(int_bytes, dtype=torch.uint8, device=self.device)
             self.host_ws = torch.empty(int_bytes, dtype=torch.uint8, pin_memory=True)
