@@ -134,10 +134,7 @@ class Runner:
             self.dt = dt
             self.o = torch.empty_like(self.q)
             self.lse = torch.empty(self.q.shape[:2], dtype=torch.float32, device="cuda")
-            self._plan()
-            t0 = time.perf_counter()
-            self._plan()
-            self.plan_us = (time.perf_counter() - t0) * 1e6
+            self.plan_us = self._time_plan()
             return
         if w.kind == "pod":
             wp, wd = w.prefill, w.decode
@@ -152,10 +149,7 @@ class Runner:
             self.ws, self.ws_p, self.ws_d = pkv.Workspace(), pkv.Workspace(), pkv.Workspace()
             self.dt = dt
             self.sequential = False     # True: the same parts as separate prefill + decode runs
-            self._plan()
-            t0 = time.perf_counter()
-            self._plan()
-            self.plan_us = (time.perf_counter() - t0) * 1e6
+            self.plan_us = self._time_plan()
             return
         if w.kind == "append":
             self.ak, self.av = dev(w.append_k), dev(w.append_v)
@@ -188,11 +182,23 @@ class Runner:
             if w.kind == "cascade":
                 self.prefix = dev_i32(w.prefix_indices)
         self.dt = dt
-        self._plan()
-        # steady-state host plan time: the second plan of the same lengths
-        t0 = time.perf_counter()
-        self._plan()
-        self.plan_us = (time.perf_counter() - t0) * 1e6
+        self.plan_us = self._time_plan()
+
+    def _time_plan(self, calls=20):
+        """Steady-state host time of one plan call (the median of `calls` calls after two
+        untimed ones, each on an idle stream): the host rule, the table writes and queuing
+        the table copy; the copy itself runs on the stream after the call returns."""
+        torch = self.torch
+        for _ in range(2):
+            self._plan()
+        times = []
+        for _ in range(calls):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            self._plan()
+            times.append(time.perf_counter() - t0)
+        torch.cuda.synchronize()
+        return float(np.median(times)) * 1e6
 
     def _plan(self):
         w, pkv, torch, dt = self.w, self.pkv, self.torch, self.dt
