@@ -240,3 +240,37 @@ def test_cpp_planner_equals_spec_with_window(lib, seed):
     assert counts[2] == spec.chunk_pages and counts[3] == spec.num_slots
     assert [tuple(r) for r in items.tolist()] == [tuple(r) for r in spec.items]
     assert [tuple(r[:5]) for r in groups.tolist()] == [tuple(g) for g in spec.merge_groups]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_cpp_planner_equals_spec_with_long_items(lib, seed):
+    """Items of up to millions of tokens (the ordering key then spans several radix digits of
+    the C++ sort), many equal lengths (ties keep the (b, tile, g, j) order), and schedules
+    that leave whole requests or quarters of the work in one item."""
+    rng = np.random.default_rng(4100 + seed)
+    B, P, Hkv, G = 24, 16, 2, 4
+    kv = np.exp2(rng.uniform(0, 24, size=B)).astype(np.int64)
+    kv[rng.random(B) < 0.3] = kv[0]                      # ties across requests
+    kv[rng.random(B) < 0.1] = 0
+    n = -(-kv // P)
+    indptr = np.zeros(B + 1, dtype=np.int32)
+    indptr[1:] = np.cumsum(n)
+    lpl = np.where(n > 0, kv - (n - 1) * P, 0).astype(np.int32)
+    qo = np.ones(B, dtype=np.int64)
+    for sched in ((1, 1, 16), (4, 1, 16), (64, 2, 16)):
+        spec = plan_spec(qo, kv, P, Hkv, G, G, False, *sched)
+        items, groups, counts = lib.pkv_plan_host(lib.PKV_KIND_DECODE, None, indptr, lpl, G * Hkv,
+                                                  Hkv, P, 0, sched)
+        assert max(it[6] - it[5] for it in spec.items) >= 1 << 11 or sched[0] == 64
+        assert counts[2] == spec.chunk_pages and counts[3] == spec.num_slots
+        assert [tuple(r) for r in items.tolist()] == [tuple(r) for r in spec.items], sched
+        assert [tuple(r[:5]) for r in groups.tolist()] == [tuple(g) for g in spec.merge_groups]
+
+
+def test_long_item_cases_reach_three_radix_digits():
+    """Some case above has an item of at least 2^22 tokens (a third 11-bit digit)."""
+    longest = 0
+    for seed in range(6):
+        rng = np.random.default_rng(4100 + seed)
+        longest = max(longest, int(np.exp2(rng.uniform(0, 24, size=24)).max()))
+    assert longest >= 1 << 22
