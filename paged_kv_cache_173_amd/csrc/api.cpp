@@ -454,7 +454,8 @@ pkv_status merge_part(const pkv_plan_part& part, bool prefill, const int32_t* qo
   m.o = o;
   m.lse = lse;
   m.sinks = sinks;
-  const hipError_t e = pkv::launch_merge_groups(m, dtype, out_kind, part.num_groups, stream);
+  const hipError_t e =
+      pkv::launch_merge_groups(m, dtype, out_kind, part.num_groups, part.num_slots, stream);
   if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
   return PKV_OK;
 }
@@ -896,7 +897,8 @@ pkv_status pkv_single_decode(const void* q, const void* k, const void* v, int32_
     m.part_lse = part_lse;
     m.o = o;
     m.lse = lse;
-    e = pkv::launch_merge_groups(m, dtype, pkv::kOutStorage, num_kv_heads, hs);
+    e = pkv::launch_merge_groups(m, dtype, pkv::kOutStorage, num_kv_heads,
+                                 static_cast<int64_t>(num_kv_heads) * nchunks, hs);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
   }
   return ok();

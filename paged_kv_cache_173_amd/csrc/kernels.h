@@ -148,8 +148,9 @@ hipError_t launch_prefill(const PrefillArgs& a, int32_t storage_dtype, OutKind o
                           PageMode mode, int32_t grid, hipStream_t stream,
                           const LaunchEvents& ev = {});
 
+// num_chunks: the chunks of all groups together (chooses the mapping).
 hipError_t launch_merge_groups(const MergeGroupsArgs& a, int32_t storage_dtype, OutKind out,
-                               int32_t num_groups, hipStream_t stream);
+                               int32_t num_groups, int64_t num_chunks, hipStream_t stream);
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 

@@ -7,9 +7,9 @@
 // sections "Attention states" and "Extreme-negative-logit correction"; docs
 // index "flashinfer.cascade" > "Merge Attention States").
 //
-// Mapping: the merge of a planned split group gives each output row a
-// workgroup whose waves split the chunks; the public merges give each row one
-// wave whose lanes stride over head_dim and read the states in ascending k.
+// Mapping: every output row gets one wave whose lanes stride over head_dim and
+// read the states in ascending k (four rows per workgroup), except the rows of
+// split groups of many chunks, whose chunks four waves share.
 // Every reduction runs in a fixed order, so a run is reproducible bit for bit.
 // The work is a few MB at most and HBM-bound; fp32 throughout, output rounded
 // once.
@@ -41,16 +41,23 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// Merge of the chunks of one planned split group: blockIdx.x = group,
-// blockIdx.y = row. The 64 lanes of every wave read the chunks' LSEs in
-// parallel (max and sum), the 4 waves split the chunks (k = wave, wave+4, ...)
-// for the weighted sum of outputs, and the four partial sums add up in LDS
-// in a fixed order, so every run gives the same bits.
-template <class OUT>
+// Merge of the chunks of one planned split group: blockIdx.x = group. With
+// WPR = 1 wave per row, wave w of blockIdx.y takes row 4 * blockIdx.y + w and
+// adds up the chunks' outputs in ascending chunk order; with WPR = 4 (groups
+// of many chunks), the four waves of blockIdx.y take row blockIdx.y and split
+// its chunks (k = w, w+4, ...), and their four partial sums add up in LDS in a
+// fixed order. Every wave reads the row's chunk LSEs with its 64 lanes in
+// parallel (max and sum); lane l owns output columns 2l and 2l+1. The output
+// loads go out in batches of kBatch chunks, the first batch before the LSE
+// reductions (which do not need it), so a wave's first kBatch chunks cost
+// about one memory round trip. Every reduction runs in a fixed order, so every
+// run gives the same bits.
+template <class OUT, int WPR>
 __global__ __launch_bounds__(256) void merge_groups_kernel(const MergeGroupsArgs a) {
   constexpr int D = kHeadDim;
-  __shared__ float s_red[4][D];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  constexpr int kBatch = 8;
+  __shared__ float s_red[WPR == 4 ? 4 : 1][D];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   int b, tile, g, sb, n;
   if (a.groups != nullptr) {
     const int32_t* gr = a.groups + 8 * blockIdx.x;
@@ -67,41 +74,75 @@ __global__ __launch_bounds__(256) void merge_groups_kernel(const MergeGroupsArgs
     sb = g * n;
   }
   const int R = a.rows_per_tile;
-  const int r = blockIdx.y;
+  const int r = WPR == 4 ? static_cast<int>(blockIdx.y) : 4 * static_cast<int>(blockIdx.y) + wave;
+  if (r >= R) return;       // WPR = 1: uniform across the wave; WPR = 4: never taken
   RowMap map{a.num_qo_heads, a.group, a.prefill != 0};
   const int64_t orow = map.out_row(a.qo_indptr, b, tile, g, r, R);
-  if (orow < 0) return;                       // uniform across the workgroup
+  if (orow < 0) return;     // uniform across the wave (WPR = 4: the workgroup)
+  // This wave's chunks: k = k_first, k_first + k_step, ...
+  const int k_first = WPR == 4 ? wave : 0;
+  constexpr int k_step = WPR == 4 ? 4 : 1;
+
+  float2 v[kBatch];
+  float lk[kBatch];
+  auto load_batch = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int k = k0 + k_step * i;
+      if (k < n) {
+        const int64_t srow = static_cast<int64_t>(sb + k) * R + r;
+        lk[i] = a.part_lse[srow];
+        v[i] = *reinterpret_cast<const float2*>(a.part_o + srow * D + 2 * lane);
+      }
+    }
+  };
+  load_batch(k_first);
 
   const float* lse = a.part_lse + static_cast<int64_t>(sb) * R + r;   // chunk k at lse[k * R]
-  float M = neg_inf();
-  for (int k = lane; k < n; k += 64) M = fmaxf(M, lse[static_cast<int64_t>(k) * R]);
+  // Lane l holds the LSE of chunk l (the first 64 chunks) for both reductions.
+  const float l0 = lane < n ? lse[static_cast<int64_t>(lane) * R] : neg_inf();
+  float M = l0;
+  for (int k = lane + 64; k < n; k += 64) M = fmaxf(M, lse[static_cast<int64_t>(k) * R]);
   M = wave_max(M);
   // An attention sink of the row's head is one more state (0, sink): it
   // enters the maximum and the sum, and adds nothing to the output.
   const float sink = a.sinks != nullptr ? a.sinks[orow % a.num_qo_heads] : neg_inf();
   M = fmaxf(M, sink);
   const float Mu = (M == neg_inf()) ? 0.f : M;
-  float L = 0.f;
-  for (int k = lane; k < n; k += 64) L += fast_exp2((lse[static_cast<int64_t>(k) * R] - Mu) * kLog2e);
+  float L = lane < n ? fast_exp2((l0 - Mu) * kLog2e) : 0.f;
+  for (int k = lane + 64; k < n; k += 64)
+    L += fast_exp2((lse[static_cast<int64_t>(k) * R] - Mu) * kLog2e);
   L = wave_sum(L) + fast_exp2((sink - Mu) * kLog2e);
 
   float o0 = 0.f, o1 = 0.f;
-  for (int k = wave; k < n; k += 4) {
-    const int64_t srow = static_cast<int64_t>(sb + k) * R + r;
-    const float w = fast_exp2((a.part_lse[srow] - Mu) * kLog2e);
-    const float2 v = *reinterpret_cast<const float2*>(a.part_o + srow * D + 2 * lane);
-    o0 += w * v.x;
-    o1 += w * v.y;
+  for (int k0 = k_first; k0 < n; k0 += k_step * kBatch) {
+    if (k0 != k_first) load_batch(k0);
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (k0 + k_step * i < n) {
+        const float w = fast_exp2((lk[i] - Mu) * kLog2e);
+        o0 += w * v[i].x;
+        o1 += w * v[i].y;
+      }
+    }
   }
-  s_red[wave][2 * lane] = o0;
-  s_red[wave][2 * lane + 1] = o1;
-  __syncthreads();
-  if (tid < D) {
-    const float sum = ((s_red[0][tid] + s_red[1][tid]) + s_red[2][tid]) + s_red[3][tid];
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    store_f(static_cast<OUT*>(a.o) + orow * D + tid, sum * inv);
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  if constexpr (WPR == 4) {
+    s_red[wave][2 * lane] = o0;
+    s_red[wave][2 * lane + 1] = o1;
+    __syncthreads();
+    const int tid = threadIdx.x;
+    if (tid < D) {
+      const float sum = ((s_red[0][tid] + s_red[1][tid]) + s_red[2][tid]) + s_red[3][tid];
+      store_f(static_cast<OUT*>(a.o) + orow * D + tid, sum * inv);
+    }
+    if (tid == 0 && a.lse != nullptr) a.lse[orow] = L > 0.f ? M + __logf(L) : neg_inf();
+  } else {
+    OUT* out = static_cast<OUT*>(a.o) + orow * D + 2 * lane;
+    store_f(out, o0 * inv);
+    store_f(out + 1, o1 * inv);
+    if (lane == 0 && a.lse != nullptr) a.lse[orow] = L > 0.f ? M + __logf(L) : neg_inf();
   }
-  if (tid == 0 && a.lse != nullptr) a.lse[orow] = L > 0.f ? M + __logf(L) : neg_inf();
 }
 
 // Generic row merge of K states: state k of row `row` is at
@@ -157,15 +198,20 @@ hipError_t merge_rows(const void* va, const float* sa, const void* vb, const flo
 }  // namespace
 
 hipError_t launch_merge_groups(const MergeGroupsArgs& a, int32_t storage_dtype, OutKind out,
-                               int32_t num_groups, hipStream_t stream) {
+                               int32_t num_groups, int64_t num_chunks, hipStream_t stream) {
   if (num_groups <= 0) return hipSuccess;
-  const dim3 grid(num_groups, a.rows_per_tile);
+  // Groups of 32 chunks or more on average: four waves per row, so that each
+  // wave has at most a quarter of the batches in a row; otherwise one wave
+  // per row (four rows per workgroup).
+  const bool split = num_chunks >= 32 * static_cast<int64_t>(num_groups);
+  const dim3 grid(num_groups, split ? a.rows_per_tile : (a.rows_per_tile + 3) / 4);
+  auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, a); };
   if (out == kOutF32) {
-    hipLaunchKernelGGL(merge_groups_kernel<float>, grid, dim3(256), 0, stream, a);
+    split ? go(merge_groups_kernel<float, 4>) : go(merge_groups_kernel<float, 1>);
   } else if (storage_dtype == 0) {
-    hipLaunchKernelGGL(merge_groups_kernel<_Float16>, grid, dim3(256), 0, stream, a);
+    split ? go(merge_groups_kernel<_Float16, 4>) : go(merge_groups_kernel<_Float16, 1>);
   } else {
-    hipLaunchKernelGGL(merge_groups_kernel<__bf16>, grid, dim3(256), 0, stream, a);
+    split ? go(merge_groups_kernel<__bf16, 4>) : go(merge_groups_kernel<__bf16, 1>);
   }
   return hipGetLastError();
 }

@@ -248,3 +248,23 @@ def test_no_variant_matches_plain_path(pkv, ws):
                                  up.kv_indices, w.sm_scale, window_left=-1, logits_soft_cap=0.0)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("regime", ["four_waves_per_row", "one_wave_per_row"])
+def test_decode_merge_of_many_chunks(pkv, ws, regime):
+    """Split groups of more than 64 chunks (the merge's LSE loops past one chunk per lane,
+    several batches of output loads) under both merge mappings: four waves sharing a row when
+    the groups average 32 chunks or more, one wave per row otherwise; with sinks."""
+    if regime == "four_waves_per_row":
+        lens = [5000, 3100]
+    else:
+        lens = [3000] + [40] * 30
+    w = wl.batch_decode(seed=350, kv_lens=lens, num_qo_heads=16, num_kv_heads=4, page_size=16,
+                        dtype="bf16", canary=True)
+    sched = (1024, 8, 16)
+    _, groups, counts = pkv.pkv_plan_host(pkv.PKV_KIND_DECODE, None, w.kv.kv_indptr,
+                                          w.kv.last_page_len, 16, 4, 16, 0, sched)
+    n = groups[:, 4]
+    assert n.max() > 64
+    assert (counts[3] >= 32 * len(n)) == (regime == "four_waves_per_row")
+    run_decode(pkv, ws, w, sinks=_sinks(351, 16), sched=sched, label=f"merge of many chunks, {regime}")
