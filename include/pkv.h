@@ -286,7 +286,9 @@ pkv_status pkv_plan_export(const pkv_plan_info* plan, const void* host_ws, int32
  * unmodified until that copy has completed. A later plan call (of any kind)
  * given the same host_ws waits for it before writing there, so one staging
  * buffer can serve every plan call; the wait covers only that copy and what
- * was queued on its stream before it. With int_ws / float_ws NULL or too small
+ * was queued on its stream before it. Plan calls that share a host_ws must
+ * not run concurrently (from several threads); calls on different host_ws
+ * may. With int_ws / float_ws NULL or too small
  * it returns WORKSPACE_TOO_SMALL, queues nothing and reports the required
  * sizes in *out.
  * run: checks that the plan matches `kv` and launches the decode kernel and,

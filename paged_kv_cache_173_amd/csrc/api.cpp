@@ -260,10 +260,16 @@ std::unordered_map<const void*, StagingCopy> g_staging;
 pkv_status claim_staging(void* host_ws, size_t host_ws_bytes, int64_t need, char** h) {
   *h = nullptr;
   if (host_ws == nullptr || host_ws_bytes < static_cast<size_t>(need)) return PKV_OK;
-  std::lock_guard<std::mutex> lock(g_staging_mu);
-  auto it = g_staging.find(host_ws);
-  if (it != g_staging.end()) {
-    const hipError_t e = hipEventSynchronize(it->second.done);
+  hipEvent_t done = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_staging_mu);
+    auto it = g_staging.find(host_ws);
+    if (it != g_staging.end()) done = it->second.done;
+  }
+  // Only a plan call on this same buffer replaces its event, and such calls
+  // do not overlap (documented), so the handle stays valid without the lock.
+  if (done != nullptr) {
+    const hipError_t e = hipEventSynchronize(done);
     if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(plan staging copy)");
   }
   *h = static_cast<char*>(host_ws);
