@@ -201,7 +201,8 @@ int32_t pkv_abi_version(void);
 size_t pkv_plan_info_size(void);
 
 /* Fill *out with defaults for `device`: num_cus = the device's CU count,
- * wg_per_cu = 4, min_chunk_tokens = 256. Needs a GPU. */
+ * wg_per_cu = 4, min_chunk_tokens = 128 (below that a chunk's fixed cost
+ * outweighs the parallelism it adds). Needs a GPU. */
 pkv_status pkv_default_sched(int32_t device, pkv_sched* out);
 
 /* Defaults tuned to one kernel: as pkv_default_sched, but wg_per_cu follows
