@@ -11,6 +11,9 @@ the next call comes:
   copy before it overwrites the shared staging buffer, so each run sees its own
   tables and its outputs equal, bit for bit, those of the same plan made on an
   idle stream;
+* the same with one plan of every kind (prefill, cascade, block-sparse, mixed
+  batch, decode) in a row on one workspace: each kind writes the shared staging
+  buffer at its own call site;
 * a plan made and run on a side stream.
 Every case prints its name first.
 """
@@ -112,3 +115,81 @@ def test_plan_and_run_on_a_side_stream(pkv, busy_operands):
         o, lse = plan_and_run(pkv, w, up, ws, stream=side)
     side.synchronize()
     assert torch.equal(bits(o), bits(ref[0])) and torch.equal(bits(lse), bits(ref[1]))
+
+
+def _kinds(pkv):
+    """(name, plan(ws), run(plan)) for one small case of every plan kind; every run returns
+    its output tensors."""
+    from gpu_common import dev, dev_i32
+    out = []
+    w = wl.batch_prefill(seed=980, batch=3, qo_min=5, qo_max=150, prefix_max=200,
+                         num_qo_heads=8, num_kv_heads=2, page_size=16, dtype="bf16")
+    up = Uploaded(w)
+    out.append(("prefill",
+                lambda ws, w=w: pkv.pkv_prefill_plan(w.qo_indptr, w.kv.kv_indptr,
+                                                     w.kv.last_page_len, 8, 2, 128, 16,
+                                                     torch.bfloat16, True, ws, sched=SPLIT),
+                lambda p, w=w, up=up: pkv.pkv_prefill_run(p, up.q, up.k, up.v, up.qo_indptr,
+                                                          up.kv_indptr, up.kv_indices,
+                                                          w.sm_scale)))
+    w = wl.cascade(seed=981, batch=4, prefix_len=300, suffix_lens=[1, 40, 0, 90],
+                   num_qo_heads=8, num_kv_heads=2, page_size=16, dtype="f16")
+    up = Uploaded(w)
+    out.append(("cascade",
+                lambda ws, w=w: pkv.pkv_cascade_plan(len(w.prefix_indices), w.prefix_last_page_len,
+                                                     w.kv.kv_indptr, w.kv.last_page_len, 8, 2, 128,
+                                                     16, torch.float16, ws),
+                lambda p, w=w, up=up: pkv.pkv_cascade_run(p, up.q, up.k, up.v, up.prefix_indices,
+                                                          up.kv_indptr, up.kv_indices,
+                                                          w.sm_scale)))
+    w = wl.block_sparse(seed=982, num_qo_tokens=150, num_kv_tokens=200, row_block=32,
+                        col_block=32, density=0.5, num_qo_heads=4, num_kv_heads=2)
+    t = (dev(w.q, w.dtype), dev(w.k, w.dtype), dev(w.v, w.dtype), dev_i32(w.bsr_indptr),
+         dev_i32(w.bsr_indices))
+    dt = torch.float16 if w.dtype == "f16" else torch.bfloat16
+    out.append(("block-sparse",
+                lambda ws, w=w, dt=dt: pkv.pkv_block_sparse_plan(
+                    w.bsr_indptr, w.bsr_indices, w.q.shape[0], w.k.shape[0], w.row_block,
+                    w.col_block, 4, 2, 128, dt, ws),
+                lambda p, w=w, t=t: pkv.pkv_block_sparse_run(p, *t, w.sm_scale)))
+    w = wl.pod(seed=983, p_batch=2, qo_min=3, qo_max=60, prefix_max=80, d_batch=3, kv_min=1,
+               kv_max=300, num_qo_heads=8, num_kv_heads=2, page_size=16, dtype="bf16")
+    wp, wd = w.prefill, w.decode
+    t = (dev(wp.kv.k_cache, wp.dtype), dev(wp.kv.v_cache, wp.dtype), dev(wp.q, wp.dtype),
+         dev_i32(wp.qo_indptr), dev_i32(wp.kv.kv_indptr), dev_i32(wp.kv.kv_indices),
+         dev(wd.q, wd.dtype), dev_i32(wd.kv.kv_indptr), dev_i32(wd.kv.kv_indices))
+    out.append(("mixed batch",
+                lambda ws, wp=wp, wd=wd: pkv.pkv_pod_plan(wp.qo_indptr, wp.kv.kv_indptr,
+                                                          wp.kv.last_page_len, True,
+                                                          wd.kv.kv_indptr, wd.kv.last_page_len,
+                                                          8, 2, 128, 16, torch.bfloat16, ws,
+                                                          sched=SPLIT),
+                lambda p, wp=wp, t=t: pkv.pkv_pod_run(p, *t, wp.sm_scale)))
+    w, up = decode_case(984, 20)
+    out.append(("decode",
+                lambda ws, w=w: pkv.pkv_decode_plan(w.kv.kv_indptr, w.kv.last_page_len, 32, 8,
+                                                    128, 16, torch.float16, ws, sched=SPLIT),
+                lambda p, w=w, up=up: pkv.pkv_decode_run(p, up.q, up.k, up.v, up.kv_indptr,
+                                                         up.kv_indices, w.sm_scale)))
+    return out
+
+
+def test_back_to_back_plans_of_every_kind_share_one_staging_buffer(pkv, busy_operands):
+    kinds = _kinds(pkv)
+    say("[case] every plan kind: references on an idle stream")
+    refs = []
+    for name, plan, run in kinds:
+        outs = run(plan(pkv.Workspace()))
+        torch.cuda.synchronize()
+        refs.append([t.clone() for t in outs])
+    say("[case] every plan kind: one workspace, busy stream")
+    ws = pkv.Workspace()
+    for name, plan, run in kinds:            # sizes the workspace for every kind
+        run(plan(ws))
+    torch.cuda.synchronize()
+    hold_stream(busy_operands)
+    got = [run(plan(ws)) for name, plan, run in kinds]
+    torch.cuda.synchronize()
+    for (name, _, _), outs, ref in zip(kinds, got, refs):
+        for i, (a, b) in enumerate(zip(outs, ref)):
+            assert torch.equal(bits(a), bits(b)), f"{name}: output {i} differs"
