@@ -5,7 +5,9 @@ Default workload: batch paged decode, GQA (64 requests, KV length uniform in
 1.25x the pages needed). A step is one run of the planned pass (decode
 kernel plus the merge of split chunks) over the whole batch; the host plan is
 made once per workload before timing and reused, as the plan/run split
-intends, and its host time is reported as plan_us.
+intends, and its host time is reported as plan_us (the median of 20 plan calls
+after warm-up, each on an idle stream; the call queues its table copy and
+returns without waiting for it).
 
 Timing: W warm-up steps, then K timed steps. Before every step a 512 MiB
 buffer is read (outside the timed events) so the 256 MB Infinity Cache holds

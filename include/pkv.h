@@ -289,7 +289,8 @@ pkv_status pkv_plan_export(const pkv_plan_info* plan, const void* host_ws, int32
  * buffer can serve every plan call; the wait covers only that copy and what
  * was queued on its stream before it. Plan calls that share a host_ws must
  * not run concurrently (from several threads); calls on different host_ws
- * may. With int_ws / float_ws NULL or too small
+ * may. The library keeps one HIP event per distinct host_ws it has copied
+ * from, for the life of the process. With int_ws / float_ws NULL or too small
  * it returns WORKSPACE_TOO_SMALL, queues nothing and reports the required
  * sizes in *out.
  * run: checks that the plan matches `kv` and launches the decode kernel and,
