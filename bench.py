@@ -14,9 +14,11 @@ buffer is read (outside the timed events) so the 256 MB Infinity Cache holds
 no KV and no dirty lines that would be written back during the step; each
 step is bracketed by HIP events on the stream the kernels run on.
 value = algorithmic bytes / mean step time. The attention kernel alone (the
-roofline figure) is timed by a second pair of events that its own dispatch
-carries (hipExtLaunchKernel), i.e. its begin and end timestamps, the same
-interval rocprofv3's kernel trace reports.
+roofline figure) is timed in a second pass of K steps by a pair of events that
+its own dispatch carries (hipExtLaunchKernel), i.e. its begin and end
+timestamps, the same interval rocprofv3's kernel trace reports; those events
+lengthen a step by a few microseconds, so the step times come from the first
+pass, which carries none.
 
 `--workload` selects another workload (single, decode, prefill, cascade,
 long); `--all` adds every workload's figures under "workloads" in the line.
@@ -338,7 +340,12 @@ class Runner:
 
 
 def time_steps(torch, runner, steps, warmup, flush):
-    """Returns (mean step ms, median step ms, mean attention-kernel ms or None, wall s)."""
+    """Returns (mean step ms, median step ms, mean attention-kernel ms or None, wall s).
+
+    The K timed steps carry only the step's own pair of events. The attention kernel's
+    time comes from a second pass of K steps in which the kernel's dispatch also carries
+    a pair of events (its begin and end timestamps); those events lengthen a step by a few
+    microseconds, so they stay out of the pass that gives the step time."""
     def evict():
         return flush.view(torch.int64).sum()
 
@@ -348,27 +355,35 @@ def time_steps(torch, runner, steps, warmup, flush):
         return torch.cuda.Event(enable_timing=True)
     for _ in range(warmup):
         evict()
-        runner.step((event(), event()) if timed_kernel else None)
+        runner.step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     starts = [event() for _ in range(steps)]
     ends = [event() for _ in range(steps)]
-    # The attention kernel's own begin / end timestamps (events carried by its dispatch).
-    k_begin = [event() for _ in range(steps)]
-    k_end = [event() for _ in range(steps)]
-    for ev in k_begin + k_end:               # create the events before the timed loop
+    for ev in starts + ends:                 # create the events before the timed loop
         ev.record(stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         evict()                              # evicts the Infinity Cache, outside the events
         starts[i].record(stream)
-        runner.step((k_begin[i], k_end[i]) if timed_kernel else None)
+        runner.step()
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    kern = [b.elapsed_time(e) for b, e in zip(k_begin, k_end)] if timed_kernel else None
+    kern = None
+    if timed_kernel:
+        k_begin = [event() for _ in range(steps)]
+        k_end = [event() for _ in range(steps)]
+        for ev in k_begin + k_end:
+            ev.record(stream)
+        torch.cuda.synchronize()
+        for i in range(steps):
+            evict()
+            runner.step((k_begin[i], k_end[i]))
+        torch.cuda.synchronize()
+        kern = [b.elapsed_time(e) for b, e in zip(k_begin, k_end)]
     return (float(np.mean(ms)), float(np.median(ms)),
             float(np.mean(kern)) if kern else None, wall)
 
