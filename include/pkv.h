@@ -182,7 +182,7 @@ typedef struct pkv_plan_info {
   void* float_ws;            /* device float workspace for partial states    */
   int64_t int_ws_required;   /* bytes (also set on WORKSPACE_TOO_SMALL)      */
   int64_t float_ws_required; /* bytes (also set on WORKSPACE_TOO_SMALL)      */
-  int64_t cascade_state_off; /* cascade: float ws offset of the two fp32 states */
+  int64_t cascade_state_off; /* cascade: float ws offset of the fp32 prefix state */
   int64_t order_off;         /* POD: int ws offset of the launch order (int32)   */
   int32_t num_blocks;        /* POD: workgroups of the mixed launch              */
   int32_t batch2;            /* POD: decode requests (batch = prefill requests)  */
@@ -400,8 +400,9 @@ pkv_status pkv_merge_states(const void* v, const float* s, int32_t n, int32_t nu
  * holding prefix_last_page_len tokens) and each has its own suffix page table.
  * Level 0 computes every request's state over the prefix in one pass that
  * reads the prefix once (all batch*Hq query rows against it, unmasked);
- * level 1 computes the state over each suffix (batch decode); the two states
- * are merged into o [batch, Hq, 128] (cache dtype) and lse [batch, Hq] or NULL.
+ * level 1 computes the suffix chunks' states (batch decode) and its merge
+ * combines each row's chunks with its prefix state into o [batch, Hq, 128]
+ * (cache dtype) and lse [batch, Hq] or NULL (three launches in all).
  * ------------------------------------------------------------------------- */
 pkv_status pkv_cascade_plan(int32_t prefix_num_pages, int32_t prefix_last_page_len,
                             const int32_t* suffix_indptr_h, const int32_t* suffix_last_page_len_h,

@@ -351,6 +351,13 @@ void fill_header(pkv_plan_info* out, pkv_kind kind, pkv_dtype dtype, int32_t bat
   out->sched = sched;
 }
 
+// The cascade's suffix level: every (request, KV head) group goes through the
+// merge, which adds the prefix state to its rows.
+pkv::PlanInput suffix_input(pkv::PlanInput in) {
+  in.group_all = true;
+  return in;
+}
+
 pkv::PlanInput make_input(const std::vector<int64_t>& qo, const std::vector<int64_t>& kv,
                           int32_t page_size, int32_t hkv, int32_t G, int32_t rows, bool causal,
                           const pkv_sched& s, int32_t window_left = -1) {
@@ -442,11 +449,13 @@ pkv::PrefillArgs prefill_args(const pkv_plan_info* plan, const pkv_plan_part& pa
   return a;
 }
 
-// Merges a part's split groups (if any) into its final rows.
+// Merges a part's split groups (if any) into its final rows, with a base
+// fp32 state of every row when base_o / base_lse are given.
 pkv_status merge_part(const pkv_plan_part& part, bool prefill, const int32_t* qo_indptr_d,
                       int32_t num_qo_heads, int32_t group, const void* int_ws, void* float_ws,
                       void* o, float* lse, const float* sinks, pkv_dtype dtype,
-                      pkv::OutKind out_kind, hipStream_t stream) {
+                      pkv::OutKind out_kind, hipStream_t stream, const float* base_o = nullptr,
+                      const float* base_lse = nullptr) {
   if (part.num_groups == 0) return PKV_OK;
   pkv::MergeGroupsArgs m{};
   m.groups = i_at(int_ws, part.groups_off);
@@ -460,6 +469,8 @@ pkv_status merge_part(const pkv_plan_part& part, bool prefill, const int32_t* qo
   m.o = o;
   m.lse = lse;
   m.sinks = sinks;
+  m.base_o = base_o;
+  m.base_lse = base_lse;
   const hipError_t e =
       pkv::launch_merge_groups(m, dtype, out_kind, part.num_groups, part.num_slots, stream);
   if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
@@ -478,14 +489,16 @@ pkv_status run_decode_part(const pkv_plan_info* plan, const pkv_plan_part& part,
                            const int32_t* kv_indices_d, float sm_scale, void* o, float* lse,
                            pkv::OutKind out_kind, hipStream_t stream,
                            const pkv::LaunchEvents& ev = {},
-                           const pkv::VariantArgs& var = kNoVariant) {
+                           const pkv::VariantArgs& var = kNoVariant,
+                           const float* base_o = nullptr, const float* base_lse = nullptr) {
   const pkv::DecodeArgs a =
       decode_args(plan, part, q, kv, kv_indptr_d, kv_indices_d, sm_scale, o, lse, var);
   const hipError_t e = pkv::launch_decode(a, plan->dtype, out_kind, page_mode(plan->page_size),
                                           part.num_items, stream, ev);
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
   return merge_part(part, false, nullptr, plan->num_qo_heads, a.group, plan->int_ws,
-                    plan->float_ws, o, lse, var.sinks, plan->dtype, out_kind, stream);
+                    plan->float_ws, o, lse, var.sinks, plan->dtype, out_kind, stream, base_o,
+                    base_lse);
 }
 
 pkv_status run_prefill_part(const pkv_plan_info* plan, const pkv_plan_part& part, const void* q,
@@ -588,7 +601,7 @@ pkv_status pkv_workspace_size(pkv_kind kind, int32_t batch, int32_t num_qo_heads
       place_counts(n, n, n, 0, 1, kRowsPerPrefillTile, 0, &lay, &part[0]);
       place_counts(n, n, n, 0, batch, G, 0, &lay, &part[1]);
       const int64_t rows = static_cast<int64_t>(batch) * num_qo_heads;
-      lay.float_bytes += 2 * (align_up(rows * head_dim * 4) + align_up(rows * 4));
+      lay.float_bytes += align_up(rows * head_dim * 4) + align_up(rows * 4);
       break;
     }
     case PKV_KIND_POD:            // batch = prefill requests + decode requests
@@ -994,8 +1007,9 @@ pkv_status pkv_cascade_plan(int32_t prefix_num_pages, int32_t prefix_last_page_l
   if (!pkv::build_plan(make_input(pre_qo, pre_len, page_size, num_kv_heads, G,
                                   kRowsPerPrefillTile, false, s0),
                        &hp0, &err) ||
-      !pkv::build_plan(make_input(suf_qo, suf_len, page_size, num_kv_heads, G, G, false, s1), &hp1,
-                       &err))
+      !pkv::build_plan(suffix_input(make_input(suf_qo, suf_len, page_size, num_kv_heads, G, G,
+                                               false, s1)),
+                       &hp1, &err))
     return fail(PKV_ERR_INVALID_ARG, err);
   fill_header(out, PKV_KIND_CASCADE, dtype, batch, num_qo_heads, num_kv_heads, head_dim,
               page_size, batch, s1);
@@ -1004,10 +1018,10 @@ pkv_status pkv_cascade_plan(int32_t prefix_num_pages, int32_t prefix_last_page_l
   lay.int_bytes = kAlign;
   place_part(hp0, 1, kRowsPerPrefillTile, 0, &lay, &out->part[0]);
   place_part(hp1, batch, G, 0, &lay, &out->part[1]);
-  // float ws: both parts' partials, then fp32 states A (prefix) and B (suffix)
+  // float ws: both parts' partials, then the fp32 prefix state of every row
   out->cascade_state_off = lay.float_bytes;
   const int64_t rows = static_cast<int64_t>(batch) * num_qo_heads;
-  lay.float_bytes += 2 * (align_up(rows * head_dim * 4) + align_up(rows * 4));
+  lay.float_bytes += align_up(rows * head_dim * 4) + align_up(rows * 4);
   char* h = nullptr;
   if ((st = claim_staging(host_ws, host_ws_bytes, lay.int_bytes, &h))) return st;
   if (h != nullptr) {
@@ -1040,22 +1054,16 @@ pkv_status pkv_cascade_run(const pkv_plan_info* plan, const void* q, const pkv_p
   const int64_t D = plan->head_dim;
   float* a_o = f_at(plan->float_ws, plan->cascade_state_off);
   float* a_lse = f_at(plan->float_ws, plan->cascade_state_off + align_up(rows * D * 4));
-  float* b_o = f_at(plan->float_ws,
-                    plan->cascade_state_off + align_up(rows * D * 4) + align_up(rows * 4));
-  float* b_lse = f_at(plan->float_ws, plan->cascade_state_off + 2 * align_up(rows * D * 4) +
-                                          align_up(rows * 4));
   const int32_t* hdr = i_at(plan->int_ws, 0);
   // Level 0: prefix state of every (request, head) row, prefix read once.
   if ((st = run_prefill_part(plan, plan->part[0], q, kv, hdr, hdr + 2, prefix_indices_d, sm_scale,
                              a_o, a_lse, plan->num_qo_heads, pkv::kOutF32, hs)))
     return st;
-  // Level 1: suffix state per request (batch decode).
+  // Level 1: suffix chunks per request (batch decode; every group is a merge
+  // group), merged with the prefix state into the final rows.
   if ((st = run_decode_part(plan, plan->part[1], q, kv, suffix_indptr_d, suffix_indices_d,
-                            sm_scale, b_o, b_lse, pkv::kOutF32, hs)))
+                            sm_scale, o, lse, pkv::kOutStorage, hs, {}, kNoVariant, a_o, a_lse)))
     return st;
-  hipError_t e = pkv::launch_merge2_f32_to(a_o, a_lse, b_o, b_lse, o, lse, rows,
-                                           static_cast<int32_t>(D), plan->dtype, hs);
-  if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
   return ok();
 }
 

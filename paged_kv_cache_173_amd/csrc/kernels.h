@@ -125,6 +125,10 @@ struct MergeGroupsArgs {
   void* o;
   float* lse;                 // or NULL
   const float* sinks;         // device [num_qo_heads] sink logits, or NULL
+  // A further fp32 state of every output row (O [out rows][D], LSE [out rows]),
+  // merged with the row's chunks, or NULL (the cascade's prefix state).
+  const float* base_o;
+  const float* base_lse;
 };
 
 // Events a launch may carry on its own dispatch packet (hipExtLaunchKernel):

@@ -108,11 +108,17 @@ __global__ __launch_bounds__(256) void merge_groups_kernel(const MergeGroupsArgs
   // enters the maximum and the sum, and adds nothing to the output.
   const float sink = a.sinks != nullptr ? a.sinks[orow % a.num_qo_heads] : neg_inf();
   M = fmaxf(M, sink);
+  // A base state of the row (the cascade's prefix) enters like one more chunk,
+  // added after the chunks.
+  const float base = a.base_lse != nullptr ? a.base_lse[orow] : neg_inf();
+  M = fmaxf(M, base);
   const float Mu = (M == neg_inf()) ? 0.f : M;
   float L = lane < n ? fast_exp2((l0 - Mu) * kLog2e) : 0.f;
   for (int k = lane + 64; k < n; k += 64)
     L += fast_exp2((lse[static_cast<int64_t>(k) * R] - Mu) * kLog2e);
   L = wave_sum(L) + fast_exp2((sink - Mu) * kLog2e);
+  const float w_base = fast_exp2((base - Mu) * kLog2e);   // 0 without a base state
+  L += w_base;
 
   float o0 = 0.f, o1 = 0.f;
   for (int k0 = k_first; k0 < n; k0 += k_step * kBatch) {
@@ -133,11 +139,17 @@ __global__ __launch_bounds__(256) void merge_groups_kernel(const MergeGroupsArgs
     __syncthreads();
     const int tid = threadIdx.x;
     if (tid < D) {
-      const float sum = ((s_red[0][tid] + s_red[1][tid]) + s_red[2][tid]) + s_red[3][tid];
+      float sum = ((s_red[0][tid] + s_red[1][tid]) + s_red[2][tid]) + s_red[3][tid];
+      if (a.base_o != nullptr) sum += w_base * a.base_o[orow * D + tid];
       store_f(static_cast<OUT*>(a.o) + orow * D + tid, sum * inv);
     }
     if (tid == 0 && a.lse != nullptr) a.lse[orow] = L > 0.f ? M + __logf(L) : neg_inf();
   } else {
+    if (a.base_o != nullptr) {
+      const float2 bv = *reinterpret_cast<const float2*>(a.base_o + orow * D + 2 * lane);
+      o0 += w_base * bv.x;
+      o1 += w_base * bv.y;
+    }
     OUT* out = static_cast<OUT*>(a.o) + orow * D + 2 * lane;
     store_f(out, o0 * inv);
     store_f(out + 1, o1 * inv);

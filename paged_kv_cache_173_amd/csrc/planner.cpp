@@ -77,7 +77,8 @@ bool build_plan(const PlanInput& in, HostPlan* out, std::string* err) {
     const int64_t n_chunks = std::max<int64_t>(1, ceil_div(te.pages, c));
     for (int32_t g = 0; g < in.num_kv_heads; ++g) {
       int64_t slot_begin = -1;
-      if (n_chunks > 1) {
+      const bool grouped = n_chunks > 1 || in.group_all;
+      if (grouped) {
         slot_begin = slot;
         MergeGroup mg{};
         mg.b = te.b;
@@ -99,7 +100,7 @@ bool build_plan(const PlanInput& in, HostPlan* out, std::string* err) {
         const int64_t k1 = std::min((te.page_lo + (j + 1) * c) * P, te.kv_end);
         it.kv_begin = static_cast<int32_t>(k0);
         it.kv_end = static_cast<int32_t>(k1);
-        it.slot = n_chunks > 1 ? static_cast<int32_t>(slot_begin + j) : -1;
+        it.slot = grouped ? static_cast<int32_t>(slot_begin + j) : -1;
         tokens[n] = static_cast<uint32_t>(k1 - k0);
         max_tokens = std::max(max_tokens, tokens[n]);
         ++n;

@@ -41,6 +41,10 @@ struct PlanInput {
   int32_t num_cus;
   int32_t wg_per_cu;
   int32_t min_chunk_tokens;
+  // Every (request, tile, KV head) group becomes a merge group with partial-
+  // state slots, also when it is one chunk (so that a merge can add a further
+  // state to every row).
+  bool group_all = false;
 };
 
 struct HostPlan {
