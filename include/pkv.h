@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 3
+#define PKV_ABI_VERSION 4
 
 typedef int32_t pkv_status;
 enum {
@@ -146,13 +146,19 @@ typedef struct pkv_sched {
 } pkv_sched;
 
 /* One planned pass (decode, prefill, or one level of a cascade). Offsets are
- * in bytes from the workspace bases recorded in pkv_plan_info. */
+ * in bytes from the workspace bases recorded in pkv_plan_info.
+ * A split group's chunks write partial states into the float workspace: per
+ * row, O (f32 [D], already normalised) and the pair (m, l) in the log2 domain
+ * (m: the row's reference exponent, a running maximum of sm_scale * log2(e) *
+ * q.k; l: the sum of 2^(x_t - m) over the chunk's keys), so that a merge can
+ * weight chunk k by l_k * 2^(m_k - M) with an exact exponent difference; the
+ * chunk's natural-log LSE is (m + log2 l) * ln 2. */
 typedef struct pkv_plan_part {
   int32_t num_items;        /* work items = workgroups launched              */
-  int32_t num_groups;       /* (request, tile, kv head) groups that split     */
+  int32_t num_groups;       /* (request, tile, kv head) merge groups          */
   int32_t chunk_pages;      /* chunk size c of the rule, in pages             */
   int32_t rows_per_tile;    /* query rows per item (G for decode, 128 prefill) */
-  int32_t num_slots;        /* partial states written by split groups         */
+  int32_t num_slots;        /* partial states written by the groups' chunks   */
   int32_t causal;
   int32_t window_left;      /* the sliding window the plan was made for (-1: none) */
   int32_t reserved;
@@ -160,7 +166,7 @@ typedef struct pkv_plan_part {
   int64_t groups_off;       /* int ws: int32 [num_groups][8]                  */
   int64_t kv_len_off;       /* int ws: int32 [batch] KV length per request    */
   int64_t part_o_off;       /* float ws: f32 [num_slots][rows_per_tile][D]    */
-  int64_t part_lse_off;     /* float ws: f32 [num_slots][rows_per_tile]       */
+  int64_t part_ml_off;      /* float ws: f32 [num_slots][rows_per_tile][2] (m, l) */
 } pkv_plan_part;
 
 /* A plan: a plain struct the caller owns (copyable, no pointers to free).
@@ -182,7 +188,6 @@ typedef struct pkv_plan_info {
   void* float_ws;            /* device float workspace for partial states    */
   int64_t int_ws_required;   /* bytes (also set on WORKSPACE_TOO_SMALL)      */
   int64_t float_ws_required; /* bytes (also set on WORKSPACE_TOO_SMALL)      */
-  int64_t cascade_state_off; /* cascade: float ws offset of the fp32 prefix state */
   int64_t order_off;         /* POD: int ws offset of the launch order (int32)   */
   int32_t num_blocks;        /* POD: workgroups of the mixed launch              */
   int32_t batch2;            /* POD: decode requests (batch = prefill requests)  */
@@ -214,7 +219,11 @@ pkv_status pkv_default_sched(int32_t device, pkv_sched* out);
 pkv_status pkv_default_sched_for(pkv_kind kind, int32_t device, pkv_sched* out);
 
 /* ---------------------------------------------------------------------------
- * Host-only planning (no GPU needed): the work-chunk rule.
+ * Host-only planning (no GPU needed): the work-chunk rule. The FlashInfer
+ * article (section "Plan and run") has the plan inspect sequence lengths and
+ * cache metadata and pick a schedule that the run then reuses, and notes
+ * (section "Purpose and scope") that one fixed schedule spreads uneven
+ * requests badly; this rule is this library's schedule.
  *
  * Rule (integer arithmetic, ceil(a/b) rounding up):
  *   rows of request b are GQA-packed (row r = query token r/G, head
@@ -233,7 +242,9 @@ pkv_status pkv_default_sched_for(pkv_kind kind, int32_t device, pkv_sched* out);
  *   longest first (descending token count, ties by ascending b, tile, g, j).
  * Outputs: items_out[num_items][8] = {b, g, tile, page_begin, page_end,
  *   kv_begin, kv_end, slot (-1 = writes the final output)};
- *   groups_out[num_groups][8] = {b, tile, g, slot_begin, num_chunks, 0, 0, 0};
+ *   groups_out[num_groups][8] = {b, tile, g, slot_begin, num_chunks,
+ *   base_slot_begin, base_num_chunks, base_row} (the last three are 0 except
+ *   in a cascade's suffix part, see pkv_cascade_plan);
  *   counts_out[4] = {num_items, num_groups, chunk_pages, num_slots}.
  * qo_indptr_h may be NULL for decode (kind PKV_KIND_DECODE, one query token
  * per request). window_left as in pkv_variant (-1: none). Returns
@@ -248,6 +259,9 @@ pkv_status pkv_plan_host(pkv_kind kind, const int32_t* qo_indptr_h, const int32_
                          int32_t* groups_out, int32_t groups_cap, int32_t* counts_out);
 
 /* Workspace sizes (bytes) that suffice for every plan of `kind` with at most
+ * `max_items` work items: the stable workspace buffers that the FlashInfer
+ * article (section "Plan and run") has a plan fill and every run reuse.
+ * Bounds for every plan of `kind` with at most
  * `max_items` work items (for the cascade and the mixed batch: both parts
  * together), whatever the lengths, so a caller can allocate once before
  * planning (graph capture, serving loops). `batch`: requests (decode,
@@ -264,8 +278,10 @@ pkv_status pkv_workspace_size(pkv_kind kind, int32_t batch, int32_t num_qo_heads
                               size_t* int_ws_bytes, size_t* float_ws_bytes,
                               size_t* host_ws_bytes);
 
-/* Copies part `part` (0; or 1, the decode part, for a cascade or mixed-batch
- * plan) of a plan's work list to the caller: items_out[num_items][8] and
+/* The plan's work list as the run uses it (the chunk boundaries the FlashInfer
+ * article, section "Plan and run", has the plan prepare), for checking and
+ * inspection. Copies part `part` (0; or 1, the decode part, for a cascade or
+ * mixed-batch plan) of a plan's work list to the caller: items_out[num_items][8] and
  * groups_out[num_groups][8] in the layout of pkv_plan_host (counts in
  * plan->part[part]). Reads the host workspace the plan was made with, which
  * must not have been reused since. No GPU call. Errors: PLAN_MISMATCH (not a
@@ -277,7 +293,10 @@ pkv_status pkv_plan_export(const pkv_plan_info* plan, const void* host_ws, int32
                            int32_t groups_cap);
 
 /* ---------------------------------------------------------------------------
- * Batch paged decode: one query token per request.
+ * Batch paged decode: one query token per request (docs index
+ * "flashinfer.decode" > "Batch Decoding"; the page walk of the FlashInfer
+ * article, section "Block-sparse cache representation"; plan and run split as
+ * in its section "Plan and run").
  *
  * plan: validates the host page-table copies, applies the rule above, writes
  * the item and group tables into host_ws (pinned memory recommended) and
@@ -294,8 +313,10 @@ pkv_status pkv_plan_export(const pkv_plan_info* plan, const void* host_ws, int32
  * it returns WORKSPACE_TOO_SMALL, queues nothing and reports the required
  * sizes in *out.
  * run: checks that the plan matches `kv` and launches the decode kernel and,
- * if any group split, the merge kernel. q [batch, Hq, 128], o like q
- * (same dtype as the cache), lse [batch, Hq] float32 or NULL.
+ * if any group split, the merge kernel (article "FlashInfer", section
+ * "Attention states"). Runs of one plan share its workspaces, so they must
+ * not overlap: queue them on one stream, or order them. q [batch, Hq, 128],
+ * o like q (same dtype as the cache), lse [batch, Hq] float32 or NULL.
  * sm_scale multiplies q.k (usually 1/sqrt(head_dim)).
  * variant (plan: only its window_left is used; run: all of it; NULL = none)
  * selects the attention variants of pkv_variant; the run returns
@@ -327,12 +348,17 @@ pkv_status pkv_decode_run_timed(const pkv_plan_info* plan, const void* q, const 
                                 void* stream, void* attention_start, void* attention_done);
 
 /* ---------------------------------------------------------------------------
- * Batch paged prefill / append: Q_b = qo_indptr[b+1]-qo_indptr[b] query
+ * Batch paged prefill / append (docs index "flashinfer.prefill" > "Batch
+ * Prefill / Append Attention"; exact attention with the causal mask, article
+ * "FlashInfer", sections "Correctness and numerical behavior" and
+ * "Extreme-negative-logit correction"): Q_b = qo_indptr[b+1]-qo_indptr[b] query
  * tokens per request, the last Q_b of its L_b keys. causal=1 applies the
  * bottom-right mask: query i sees key t iff t <= i + L_b - Q_b (rows with no
  * visible key give O = 0, LSE = -inf). causal=0 lets every query see all L_b
  * keys. q / o [total_qo, Hq, 128], lse [total_qo, Hq] float32 or NULL.
- * Plan, workspace and variant rules as for decode. Needs G <= 128.
+ * Plan, workspace and variant rules as for decode; the run launches the
+ * prefill kernel and, if a group split, a merge kernel for the split groups.
+ * Needs G <= 128.
  * ------------------------------------------------------------------------- */
 pkv_status pkv_prefill_plan(const int32_t* qo_indptr_h, const int32_t* kv_indptr_h,
                             const int32_t* last_page_len_h, int32_t batch, int32_t num_qo_heads,
@@ -356,13 +382,17 @@ pkv_status pkv_prefill_run_timed(const pkv_plan_info* plan, const void* q, const
                                  void* attention_start, void* attention_done);
 
 /* ---------------------------------------------------------------------------
- * Single-request decode over a contiguous NHD cache k, v [kv_len, Hkv, 128]
- * (token stride Hkv*128): q [Hq, 128] -> o [Hq, 128], lse [Hq] or NULL.
- * The same chunk rule runs on the host with no device tables: chunks are
- * uniform so items are derived from the workgroup index. float_ws must hold
- * the partial states: Hq * (128 + 1) * 4 * ceil(kv_len / (c*16)) bytes at
- * most, reported via float_ws_required when too small (pass NULL, 0 to
- * query). The contiguous cache is handled as 16-token pages.
+ * Single-request decode over a contiguous NHD cache (the page "FlashInfer: A
+ * Kernel Library That Puts Attention, GEMM, and MoE Behind One API", section
+ * "Installation Paths", shows single_decode_with_kv_cache as the first call;
+ * docs index "flashinfer.decode" > "Single Request Decoding"):
+ * k, v [kv_len, Hkv, 128] (token stride Hkv*128), q [Hq, 128] -> o [Hq, 128],
+ * lse [Hq] or NULL. The same chunk rule runs on the host with no device
+ * tables: chunks are uniform, so items are derived from the workgroup index;
+ * a split KV head is merged by a second launch. float_ws holds the partial
+ * states: float_ws_required bytes (pass NULL, 0 to query; 0 when nothing
+ * splits); calls that share a workspace must not overlap. The contiguous
+ * cache is handled as 16-token pages.
  * ------------------------------------------------------------------------- */
 pkv_status pkv_single_decode(const void* q, const void* k, const void* v, int32_t kv_len,
                              int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
@@ -399,10 +429,15 @@ pkv_status pkv_merge_states(const void* v, const float* s, int32_t n, int32_t nu
  * one prefix page list (prefix_indices_h/_d, prefix_num_pages pages, the last
  * holding prefix_last_page_len tokens) and each has its own suffix page table.
  * Level 0 computes every request's state over the prefix in one pass that
- * reads the prefix once (all batch*Hq query rows against it, unmasked);
- * level 1 computes the suffix chunks' states (batch decode) and its merge
- * combines each row's chunks with its prefix state into o [batch, Hq, 128]
- * (cache dtype) and lse [batch, Hq] or NULL (three launches in all).
+ * reads the prefix once (all batch*Hq query rows against it, unmasked, the
+ * prefix split into chunks) and leaves the chunks' partial states in float_ws;
+ * level 1 is a batch decode over the suffixes in which every (request, KV
+ * head) group writes partial states, and one merge combines each group's
+ * prefix states (base_slot_begin, base_num_chunks, base_row of its group
+ * record: the level-0 slots and first row that hold its rows) with its suffix
+ * chunks into o [batch, Hq, 128] (cache dtype) and lse [batch, Hq] or NULL.
+ * Three launches in all. Runs of one plan must not overlap (see
+ * pkv_decode_run).
  * ------------------------------------------------------------------------- */
 pkv_status pkv_cascade_plan(int32_t prefix_num_pages, int32_t prefix_last_page_len,
                             const int32_t* suffix_indptr_h, const int32_t* suffix_last_page_len_h,

@@ -201,8 +201,8 @@ struct Layout {
 };
 
 // Places one part's tables (items, merge groups: 8 int32 each; KV lengths:
-// batch int32) and partial states (num_slots slots of rows_per_tile rows) at
-// the current end of each workspace.
+// batch int32) and partial states (num_slots slots of rows_per_tile rows: O
+// [128] and (m, l)) at the current end of each workspace.
 void place_counts(int64_t num_items, int64_t num_groups, int64_t num_slots, int32_t chunk_pages,
                   int64_t batch, int32_t rows_per_tile, int32_t causal, Layout* lay,
                   pkv_plan_part* part, int32_t window_left = -1) {
@@ -222,8 +222,8 @@ void place_counts(int64_t num_items, int64_t num_groups, int64_t num_slots, int3
   part->part_o_off = lay->float_bytes;
   lay->float_bytes =
       align_up(lay->float_bytes + num_slots * rows_per_tile * pkv::kHeadDimSupported * 4);
-  part->part_lse_off = lay->float_bytes;
-  lay->float_bytes = align_up(lay->float_bytes + num_slots * rows_per_tile * 4);
+  part->part_ml_off = lay->float_bytes;
+  lay->float_bytes = align_up(lay->float_bytes + num_slots * rows_per_tile * 8);
 }
 
 void place_part(const pkv::HostPlan& hp, int64_t batch, int32_t rows_per_tile, int32_t causal,
@@ -351,9 +351,9 @@ void fill_header(pkv_plan_info* out, pkv_kind kind, pkv_dtype dtype, int32_t bat
   out->sched = sched;
 }
 
-// The cascade's suffix level: every (request, KV head) group goes through the
-// merge, which adds the prefix state to its rows.
-pkv::PlanInput suffix_input(pkv::PlanInput in) {
+// Both cascade levels: every group writes partial states, which the level-1
+// merge combines (each suffix group with its prefix states).
+pkv::PlanInput all_groups(pkv::PlanInput in) {
   in.group_all = true;
   return in;
 }
@@ -411,7 +411,7 @@ pkv::DecodeArgs decode_args(const pkv_plan_info* plan, const pkv_plan_part& part
   a.o = o;
   a.lse = lse;
   a.part_o = f_at(plan->float_ws, part.part_o_off);
-  a.part_lse = f_at(plan->float_ws, part.part_lse_off);
+  a.part_ml = f_at(plan->float_ws, part.part_ml_off);
   a.kv_lens = i_at(plan->int_ws, part.kv_len_off);
   a.var = var;
   return a;
@@ -444,18 +444,25 @@ pkv::PrefillArgs prefill_args(const pkv_plan_info* plan, const pkv_plan_part& pa
   a.o = o;
   a.lse = lse;
   a.part_o = f_at(plan->float_ws, part.part_o_off);
-  a.part_lse = f_at(plan->float_ws, part.part_lse_off);
+  a.part_ml = f_at(plan->float_ws, part.part_ml_off);
   a.var = var;
   return a;
 }
 
-// Merges a part's split groups (if any) into its final rows, with a base
-// fp32 state of every row when base_o / base_lse are given.
+// The prefix states a cascade's suffix merge adds (none elsewhere).
+struct BaseStates {
+  const float* o = nullptr;
+  const float* ml = nullptr;
+  int32_t rows = 0;
+  int32_t tile_slots = 0;
+  int64_t states_per_group = 0;
+};
+
+// Merges a part's split groups (if any) into its final rows.
 pkv_status merge_part(const pkv_plan_part& part, bool prefill, const int32_t* qo_indptr_d,
                       int32_t num_qo_heads, int32_t group, const void* int_ws, void* float_ws,
                       void* o, float* lse, const float* sinks, pkv_dtype dtype,
-                      pkv::OutKind out_kind, hipStream_t stream, const float* base_o = nullptr,
-                      const float* base_lse = nullptr) {
+                      pkv::OutKind out_kind, hipStream_t stream, const BaseStates& base = {}) {
   if (part.num_groups == 0) return PKV_OK;
   pkv::MergeGroupsArgs m{};
   m.groups = i_at(int_ws, part.groups_off);
@@ -465,14 +472,16 @@ pkv_status merge_part(const pkv_plan_part& part, bool prefill, const int32_t* qo
   m.prefill = prefill ? 1 : 0;
   m.qo_indptr = qo_indptr_d;
   m.part_o = f_at(float_ws, part.part_o_off);
-  m.part_lse = f_at(float_ws, part.part_lse_off);
+  m.part_ml = f_at(float_ws, part.part_ml_off);
   m.o = o;
   m.lse = lse;
   m.sinks = sinks;
-  m.base_o = base_o;
-  m.base_lse = base_lse;
-  const hipError_t e =
-      pkv::launch_merge_groups(m, dtype, out_kind, part.num_groups, part.num_slots, stream);
+  m.base_o = base.o;
+  m.base_ml = base.ml;
+  m.base_rows = base.rows;
+  m.base_tile_slots = base.tile_slots;
+  const int64_t states = part.num_slots + base.states_per_group * part.num_groups;
+  const hipError_t e = pkv::launch_merge_groups(m, dtype, out_kind, part.num_groups, states, stream);
   if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
   return PKV_OK;
 }
@@ -483,36 +492,40 @@ pkv::LaunchEvents launch_events(void* start, void* stop) {
   return {static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop)};
 }
 
-// Launches one decode pass (items + merge) writing final rows to o / lse.
+// Launches one decode pass (items, then the merge of split groups) writing
+// final rows to o / lse.
 pkv_status run_decode_part(const pkv_plan_info* plan, const pkv_plan_part& part, const void* q,
                            const pkv_paged_kv* kv, const int32_t* kv_indptr_d,
                            const int32_t* kv_indices_d, float sm_scale, void* o, float* lse,
                            pkv::OutKind out_kind, hipStream_t stream,
                            const pkv::LaunchEvents& ev = {},
                            const pkv::VariantArgs& var = kNoVariant,
-                           const float* base_o = nullptr, const float* base_lse = nullptr) {
+                           const BaseStates& base = {}) {
   const pkv::DecodeArgs a =
       decode_args(plan, part, q, kv, kv_indptr_d, kv_indices_d, sm_scale, o, lse, var);
   const hipError_t e = pkv::launch_decode(a, plan->dtype, out_kind, page_mode(plan->page_size),
                                           part.num_items, stream, ev);
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
   return merge_part(part, false, nullptr, plan->num_qo_heads, a.group, plan->int_ws,
-                    plan->float_ws, o, lse, var.sinks, plan->dtype, out_kind, stream, base_o,
-                    base_lse);
+                    plan->float_ws, o, lse, var.sinks, plan->dtype, out_kind, stream, base);
 }
 
+// Launches one prefill pass and, when `merge` is set, the merge of its split
+// groups into o / lse (the cascade's level 0 leaves its chunk states for the
+// level-1 merge instead).
 pkv_status run_prefill_part(const pkv_plan_info* plan, const pkv_plan_part& part, const void* q,
                             const pkv_paged_kv* kv, const int32_t* qo_indptr_d,
                             const int32_t* kv_indptr_d, const int32_t* kv_indices_d,
                             float sm_scale, void* o, float* lse, int32_t num_qo_heads,
                             pkv::OutKind out_kind, hipStream_t stream,
                             const pkv::LaunchEvents& ev = {},
-                            const pkv::VariantArgs& var = kNoVariant) {
+                            const pkv::VariantArgs& var = kNoVariant, bool merge = true) {
   const pkv::PrefillArgs a = prefill_args(plan, part, q, kv, qo_indptr_d, kv_indptr_d,
                                           kv_indices_d, sm_scale, o, lse, num_qo_heads, var);
   const hipError_t e = pkv::launch_prefill(a, plan->dtype, out_kind, page_mode(plan->page_size),
                                            part.num_items, stream, ev);
   if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
+  if (!merge) return PKV_OK;
   return merge_part(part, true, qo_indptr_d, num_qo_heads, a.group, plan->int_ws, plan->float_ws,
                     o, lse, var.sinks, plan->dtype, out_kind, stream);
 }
@@ -600,8 +613,6 @@ pkv_status pkv_workspace_size(pkv_kind kind, int32_t batch, int32_t num_qo_heads
       lay.int_bytes = kAlign;
       place_counts(n, n, n, 0, 1, kRowsPerPrefillTile, 0, &lay, &part[0]);
       place_counts(n, n, n, 0, batch, G, 0, &lay, &part[1]);
-      const int64_t rows = static_cast<int64_t>(batch) * num_qo_heads;
-      lay.float_bytes += align_up(rows * head_dim * 4) + align_up(rows * 4);
       break;
     }
     case PKV_KIND_POD:            // batch = prefill requests + decode requests
@@ -867,10 +878,11 @@ pkv_status pkv_single_decode(const void* q, const void* k, const void* v, int32_
   const int64_t n_pages = (static_cast<int64_t>(kv_len) + kVirtualPage - 1) / kVirtualPage;
   const int64_t c = hp.chunk_pages;
   const int32_t nchunks = static_cast<int32_t>(std::max<int64_t>(1, (n_pages + c - 1) / c));
-  const int64_t need =
-      nchunks > 1 ? align_up(static_cast<int64_t>(num_kv_heads) * nchunks * G * head_dim * 4) +
-                        static_cast<int64_t>(num_kv_heads) * nchunks * G * 4
-                  : 0;
+  // float_ws: the partial states O [Hkv * nchunks][G][128] and (m, l)
+  // [Hkv * nchunks][G][2].
+  const int64_t slots = static_cast<int64_t>(num_kv_heads) * nchunks;
+  const int64_t o_bytes = align_up(slots * G * head_dim * 4);
+  const int64_t need = nchunks > 1 ? o_bytes + slots * G * 8 : 0;
   if (float_ws_required != nullptr) *float_ws_required = need;
   if (need > 0 && (float_ws == nullptr || float_ws_bytes < static_cast<size_t>(need)))
     return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "float workspace too small: need " +
@@ -897,13 +909,10 @@ pkv_status pkv_single_decode(const void* q, const void* k, const void* v, int32_
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.o = o;
   a.lse = lse;
-  float* part_o = static_cast<float*>(float_ws);
-  float* part_lse =
-      nchunks > 1 ? f_at(float_ws, align_up(static_cast<int64_t>(num_kv_heads) * nchunks * G *
-                                            head_dim * 4))
-                  : nullptr;
-  a.part_o = part_o;
-  a.part_lse = part_lse;
+  if (nchunks > 1) {
+    a.part_o = static_cast<float*>(float_ws);
+    a.part_ml = f_at(float_ws, o_bytes);
+  }
   hipError_t e = pkv::launch_decode(a, dtype, pkv::kOutStorage, pkv::kContiguous,
                                     num_kv_heads * nchunks, hs);
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
@@ -915,12 +924,11 @@ pkv_status pkv_single_decode(const void* q, const void* k, const void* v, int32_
     m.num_qo_heads = num_qo_heads;
     m.group = G;
     m.prefill = 0;
-    m.part_o = part_o;
-    m.part_lse = part_lse;
+    m.part_o = a.part_o;
+    m.part_ml = a.part_ml;
     m.o = o;
     m.lse = lse;
-    e = pkv::launch_merge_groups(m, dtype, pkv::kOutStorage, num_kv_heads,
-                                 static_cast<int64_t>(num_kv_heads) * nchunks, hs);
+    e = pkv::launch_merge_groups(m, dtype, pkv::kOutStorage, num_kv_heads, slots, hs);
     if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
   }
   return ok();
@@ -1004,13 +1012,26 @@ pkv_status pkv_cascade_plan(int32_t prefix_num_pages, int32_t prefix_last_page_l
   std::vector<int64_t> pre_qo(1, batch), suf_qo(batch, 1);
   pkv::HostPlan hp0, hp1;
   std::string err;
-  if (!pkv::build_plan(make_input(pre_qo, pre_len, page_size, num_kv_heads, G,
-                                  kRowsPerPrefillTile, false, s0),
+  if (!pkv::build_plan(all_groups(make_input(pre_qo, pre_len, page_size, num_kv_heads, G,
+                                             kRowsPerPrefillTile, false, s0)),
                        &hp0, &err) ||
-      !pkv::build_plan(suffix_input(make_input(suf_qo, suf_len, page_size, num_kv_heads, G, G,
-                                               false, s1)),
+      !pkv::build_plan(all_groups(make_input(suf_qo, suf_len, page_size, num_kv_heads, G, G,
+                                             false, s1)),
                        &hp1, &err))
     return fail(PKV_ERR_INVALID_ARG, err);
+  // Level 0 is one request, unmasked: every (tile, g) group has the same
+  // chunks, and group (tile, g) owns slots (tile * Hkv + g) * n0 ... Suffix
+  // group (b, g) merges the prefix states of its G rows: packed rows b*G ..
+  // b*G + G - 1 of KV head g at level 0 (the query token of request b is
+  // level-0 query token b).
+  const int32_t n0 = hp0.groups.empty() ? 0 : hp0.groups[0].num_chunks;
+  for (pkv::MergeGroup& mg : hp1.groups) {
+    const int64_t packed = static_cast<int64_t>(mg.b) * G;
+    const int64_t tile = packed / kRowsPerPrefillTile;
+    mg.base_slot_begin = static_cast<int32_t>((tile * num_kv_heads + mg.g) * n0);
+    mg.base_num_chunks = n0;
+    mg.base_row = static_cast<int32_t>(packed % kRowsPerPrefillTile);
+  }
   fill_header(out, PKV_KIND_CASCADE, dtype, batch, num_qo_heads, num_kv_heads, head_dim,
               page_size, batch, s1);
   Layout lay;
@@ -1018,10 +1039,6 @@ pkv_status pkv_cascade_plan(int32_t prefix_num_pages, int32_t prefix_last_page_l
   lay.int_bytes = kAlign;
   place_part(hp0, 1, kRowsPerPrefillTile, 0, &lay, &out->part[0]);
   place_part(hp1, batch, G, 0, &lay, &out->part[1]);
-  // float ws: both parts' partials, then the fp32 prefix state of every row
-  out->cascade_state_off = lay.float_bytes;
-  const int64_t rows = static_cast<int64_t>(batch) * num_qo_heads;
-  lay.float_bytes += align_up(rows * head_dim * 4) + align_up(rows * 4);
   char* h = nullptr;
   if ((st = claim_staging(host_ws, host_ws_bytes, lay.int_bytes, &h))) return st;
   if (h != nullptr) {
@@ -1050,19 +1067,25 @@ pkv_status pkv_cascade_run(const pkv_plan_info* plan, const void* q, const pkv_p
     return fail(PKV_ERR_INVALID_ARG, "q, o, prefix / suffix tables must be non-NULL");
   if (!aligned16(q) || !aligned16(o)) return fail(PKV_ERR_INVALID_ARG, "q / o must be 16-byte aligned");
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  const int64_t rows = static_cast<int64_t>(plan->batch) * plan->num_qo_heads;
-  const int64_t D = plan->head_dim;
-  float* a_o = f_at(plan->float_ws, plan->cascade_state_off);
-  float* a_lse = f_at(plan->float_ws, plan->cascade_state_off + align_up(rows * D * 4));
   const int32_t* hdr = i_at(plan->int_ws, 0);
-  // Level 0: prefix state of every (request, head) row, prefix read once.
+  // Level 0: the prefix's chunk states of every (request, head) row, the
+  // prefix read once; every item writes a partial state.
   if ((st = run_prefill_part(plan, plan->part[0], q, kv, hdr, hdr + 2, prefix_indices_d, sm_scale,
-                             a_o, a_lse, plan->num_qo_heads, pkv::kOutF32, hs)))
+                             nullptr, nullptr, plan->num_qo_heads, pkv::kOutStorage, hs, {},
+                             kNoVariant, /*merge=*/false)))
     return st;
-  // Level 1: suffix chunks per request (batch decode; every group is a merge
-  // group), merged with the prefix state into the final rows.
+  // Level 1: the suffix chunks per request (batch decode, every group a merge
+  // group), then one merge of each group's prefix states and suffix chunks.
+  const pkv_plan_part& p0 = plan->part[0];
+  const int32_t n0 = p0.num_groups > 0 ? p0.num_slots / p0.num_groups : 0;
+  BaseStates base;
+  base.o = f_at(plan->float_ws, p0.part_o_off);
+  base.ml = f_at(plan->float_ws, p0.part_ml_off);
+  base.rows = p0.rows_per_tile;
+  base.tile_slots = plan->num_kv_heads * n0;
+  base.states_per_group = n0;
   if ((st = run_decode_part(plan, plan->part[1], q, kv, suffix_indptr_d, suffix_indices_d,
-                            sm_scale, o, lse, pkv::kOutStorage, hs, {}, kNoVariant, a_o, a_lse)))
+                            sm_scale, o, lse, pkv::kOutStorage, hs, {}, kNoVariant, base)))
     return st;
   return ok();
 }

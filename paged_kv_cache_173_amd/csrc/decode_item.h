@@ -6,7 +6,7 @@
 // What it computes: for one work item (request b, KV head g, KV token range
 // [t0, t1)) the attention state of the G query heads of group g over those
 // tokens, with an online (running-max) softmax; a whole range gives the final
-// output, a chunk gives a partial (O, LSE) state that the merge kernel
+// output, a chunk gives a partial state (O, m, l) that the merge kernel
 // combines (FlashInfer article, sections "Attention states" and
 // "Extreme-negative-logit correction"; the page walk follows the page-table
 // layout of the docs index, "KV-Cache Layout in FlashInfer").
@@ -187,7 +187,13 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int g, i
   };
   auto softmax_pv = [&](int blk, f32x4 s, const u32x4* vc) {
     const int tb = t0 + kBlock * blk;
-    float x[4];
+    // Raw scores (soft-capped for the variant), -inf where masked. The block
+    // maximum is taken on them and scaled once, and each weight is
+    // 2^(s * scale_log2 - m) from one fused multiply-add: no rounded product
+    // of a large score with the scale enters a weight, so weights stay exact
+    // to fp32 rounding of their own (small) exponent even when every logit is
+    // ~1e5 in magnitude.
+    float r[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = tb + 4 * grp + i;
@@ -197,16 +203,16 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int g, i
         if (capped) si = soft_cap(si, a.var.cap_in, a.var.cap_out);
         vis = vis && t >= wlo;
       }
-      x[i] = vis ? si * a.scale_log2 : neg_inf();
+      r[i] = vis ? si : neg_inf();
     }
-    float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    bm = max_across_rows(bm);
+    float bm = fmaxf(fmaxf(r[0], r[1]), fmaxf(r[2], r[3]));
+    bm = max_across_rows(bm) * a.scale_log2;
     const float m_new = fmaxf(m_run, bm);
     const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
     float p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(x[i] - m_use);
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(r[i], a.scale_log2, -m_use));
     l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
     m_run = m_new;
     // Rescale only when some head's running max moved (wave-uniform branch).
@@ -300,15 +306,17 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int g, i
   __syncthreads();
 
   const int64_t row0 = static_cast<int64_t>(b) * a.num_qo_heads + g * G;
+  const bool split = slot >= 0;
   for (int e = tid; e < G * D; e += 256) {
     const int row = e >> 7, d = e & (D - 1);
     float M = lds.m[row];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) M = fmaxf(M, lds.m[w * 16 + row]);
-    // A sink (log2 domain) is one more term of the sum, with a zero value.
+    // A sink (log2 domain) is one more term of the sum, with a zero value;
+    // a split item leaves it to the merge.
     float sink = neg_inf();
     if constexpr (VAR) {
-      if (a.var.sinks != nullptr && slot < 0) sink = a.var.sinks[g * G + row] * kLog2e;
+      if (a.var.sinks != nullptr && !split) sink = a.var.sinks[g * G + row] * kLog2e;
       M = fmaxf(M, sink);
     }
     const float Mu = (M == neg_inf()) ? 0.f : M;
@@ -321,13 +329,16 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int g, i
       O += f * lds.acc_of(w)[acc_at(row, d)];
     }
     const float o = L > 0.f ? O / L : 0.f;
-    const float lse = L > 0.f ? (M + fast_log2(L)) * kLn2 : neg_inf();
-    if (slot < 0) {
+    if (!split) {
+      const float lse = L > 0.f ? (M + fast_log2(L)) * kLn2 : neg_inf();
       static_cast<OUT*>(a.o)[(row0 + row) * D + d] = out_cast<OUT>(o);
       if (d == 0 && a.lse != nullptr) a.lse[row0 + row] = lse;
     } else {
-      a.part_o[(static_cast<int64_t>(slot) * G + row) * D + d] = o;
-      if (d == 0) a.part_lse[static_cast<int64_t>(slot) * G + row] = lse;
+      // The chunk's partial state: O, and (m, l) = the reference exponent and
+      // the weight sum in the log2 domain.
+      const int64_t srow = static_cast<int64_t>(slot) * G + row;
+      a.part_o[srow * D + d] = o;
+      if (d == 0) *reinterpret_cast<f32x2*>(a.part_ml + 2 * srow) = f32x2{M, L};
     }
   }
 }

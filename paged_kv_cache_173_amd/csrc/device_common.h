@@ -154,6 +154,18 @@ __device__ __forceinline__ float sum_across_halves(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Across all 64 lanes (butterfly order: the same bits on every run).
+__device__ __forceinline__ float wave_reduce_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ float wave_reduce_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
 // Row mapping of a planned group to output rows: decode rows are the G query
 // heads of one request; prefill rows are GQA-packed (row r of a request is
 // query token r / G, head g*G + r % G).

@@ -38,6 +38,24 @@ inline bool variant_on(const VariantArgs& v) {
   return v.window_left >= 0 || v.cap_out > 0.f || v.sinks != nullptr;
 }
 
+// A split-KV partial state, as the kernels write it: for each row, O (fp32
+// [128], already divided by l) and the pair (m, l) in the log2 domain: m a
+// reference exponent (the row's running maximum of sm_scale * log2(e) * q.k),
+// l = sum over the chunk's keys of 2^(x_t - m). The row's natural-log LSE is
+// (m + log2 l) * ln 2; keeping m and l apart instead lets a merge weight the
+// chunk by l * 2^(m - M) with m - M exact, so states stay exact to fp32
+// rounding even when every logit is ~1e5 in magnitude. An empty chunk is
+// (O = 0, m = -inf, l = 0).
+//
+// Merge group record (int32[8]) of a plan part: {b, tile, g, slot_begin,
+// num_chunks, base_slot_begin, base_num_chunks, base_row}: the group's chunks
+// are slots slot_begin .. slot_begin + num_chunks - 1 of the part; a cascade's
+// suffix group also merges base_num_chunks states of the prefix part
+// (slots base_slot_begin.., rows base_row.. of each), before its own chunks. Its
+// rows may run past the prefix tile's last row; row base_row + r >= base_rows
+// is row base_row + r - base_rows of the next tile, whose slots start
+// base_tile_slots later.
+
 struct DecodeArgs {
   const void* q;            // [batch, Hq, 128] storage dtype
   const void* k;            // K page pool base
@@ -56,7 +74,7 @@ struct DecodeArgs {
   void* o;                    // final output rows [batch*Hq][128]
   float* lse;                 // final LSE [batch*Hq] or NULL
   float* part_o;              // partial states [slot][G][128]
-  float* part_lse;            // [slot][G]
+  float* part_ml;             // [slot][G][2]: (m, l)
   const int32_t* kv_lens;     // device [batch] KV length per request (variants only)
   VariantArgs var;
 };
@@ -80,7 +98,7 @@ struct PrefillArgs {
   void* o;                    // final output rows [total_qo*Hq][128]
   float* lse;                 // [total_qo*Hq] or NULL
   float* part_o;              // [slot][128 rows][128]
-  float* part_lse;            // [slot][128 rows]
+  float* part_ml;             // [slot][128 rows][2]: (m, l)
   VariantArgs var;
 };
 
@@ -113,7 +131,8 @@ struct PodArgs {
 };
 
 struct MergeGroupsArgs {
-  const int32_t* groups;      // device [num_groups][8], or NULL: implicit (single decode)
+  const int32_t* groups;      // device [num_groups][8], or NULL: implicit (single decode:
+                              // group g = KV head g, chunks in slots g*n .. g*n + n - 1)
   int32_t implicit_nchunks;
   int32_t rows_per_tile;      // rows per partial slot
   int32_t num_qo_heads;
@@ -121,14 +140,16 @@ struct MergeGroupsArgs {
   int32_t prefill;            // row mapping: 0 decode, 1 GQA-packed prefill rows
   const int32_t* qo_indptr;   // device, prefill mapping only
   const float* part_o;
-  const float* part_lse;
+  const float* part_ml;
   void* o;
   float* lse;                 // or NULL
   const float* sinks;         // device [num_qo_heads] sink logits, or NULL
-  // A further fp32 state of every output row (O [out rows][D], LSE [out rows]),
-  // merged with the row's chunks, or NULL (the cascade's prefix state).
+  // The cascade: partial states of the prefix part (slots of base_rows rows),
+  // merged before each group's own chunks (see the group record), or NULL.
   const float* base_o;
-  const float* base_lse;
+  const float* base_ml;
+  int32_t base_rows;
+  int32_t base_tile_slots;    // slots from a prefix tile's group to the next tile's
 };
 
 // Events a launch may carry on its own dispatch packet (hipExtLaunchKernel):

@@ -9,7 +9,9 @@
 //
 // Mapping: every output row gets one wave whose lanes stride over head_dim and
 // read the states in ascending k (four rows per workgroup), except the rows of
-// split groups of many chunks, whose chunks four waves share.
+// split groups of many chunks, whose chunks four waves share. The planned
+// merges read the kernels' split-KV partial states, (O, m, l) in the log2
+// domain (kernels.h); the public merges take natural-log LSEs.
 // Every reduction runs in a fixed order, so a run is reproducible bit for bit.
 // The work is a few MB at most and HBM-bound; fp32 throughout, output rounded
 // once.
@@ -30,25 +32,19 @@ __device__ __forceinline__ void store_f(OUT* p, float x) {
   *p = static_cast<OUT>(x);
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-  return x;
-}
-
-// Merge of the chunks of one planned split group: blockIdx.x = group. With
-// WPR = 1 wave per row, wave w of blockIdx.y takes row 4 * blockIdx.y + w and
-// adds up the chunks' outputs in ascending chunk order; with WPR = 4 (groups
-// of many chunks), the four waves of blockIdx.y take row blockIdx.y and split
-// its chunks (k = w, w+4, ...), and their four partial sums add up in LDS in a
-// fixed order. Every wave reads the row's chunk LSEs with its 64 lanes in
-// parallel (max and sum); lane l owns output columns 2l and 2l+1. The output
-// loads go out in batches of kBatch chunks, the first batch before the LSE
+// Merge of the chunks of one planned split group: blockIdx.x = group. Chunk k
+// of row r is the partial state (O_k, m_k, l_k) in slot sb + k (log2 domain,
+// see kernels.h): w_k = l_k 2^(m_k - M), M = max_k m_k. A cascade's suffix
+// group merges the prefix states of its rows first (states k < bn), then its
+// own chunks: the level-0 pass leaves one state per prefix chunk, so no
+// separate merge of the prefix runs.
+// With WPR = 1 wave per row, wave w of blockIdx.y takes row 4 * blockIdx.y + w
+// and adds up the chunks' outputs in ascending chunk order; with WPR = 4
+// (groups of many chunks), the four waves of blockIdx.y take row blockIdx.y
+// and split its chunks (k = w, w+4, ...), and their four partial sums add up
+// in LDS in a fixed order. Every wave reads the row's (m_k, l_k) with its 64
+// lanes in parallel (max and sum); lane l owns output columns 2l and 2l+1. The
+// output loads go out in batches of kBatch chunks, the first batch before the
 // reductions (which do not need it), so a wave's first kBatch chunks cost
 // about one memory round trip. Every reduction runs in a fixed order, so every
 // run gives the same bits.
@@ -58,7 +54,7 @@ __global__ __launch_bounds__(256) void merge_groups_kernel(const MergeGroupsArgs
   constexpr int kBatch = 8;
   __shared__ float s_red[WPR == 4 ? 4 : 1][D];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  int b, tile, g, sb, n;
+  int b = 0, tile = 0, g, sb, n, bsb = 0, bn = 0, brow = 0;
   if (a.groups != nullptr) {
     const int32_t* gr = a.groups + 8 * blockIdx.x;
     b = gr[0];
@@ -66,9 +62,10 @@ __global__ __launch_bounds__(256) void merge_groups_kernel(const MergeGroupsArgs
     g = gr[2];
     sb = gr[3];
     n = gr[4];
+    bsb = gr[5];
+    bn = gr[6];
+    brow = gr[7];
   } else {
-    b = 0;
-    tile = 0;
     g = blockIdx.x;
     n = a.implicit_nchunks;
     sb = g * n;
@@ -79,81 +76,86 @@ __global__ __launch_bounds__(256) void merge_groups_kernel(const MergeGroupsArgs
   RowMap map{a.num_qo_heads, a.group, a.prefill != 0};
   const int64_t orow = map.out_row(a.qo_indptr, b, tile, g, r, R);
   if (orow < 0) return;     // uniform across the wave (WPR = 4: the workgroup)
-  // This wave's chunks: k = k_first, k_first + k_step, ...
+  // State k of the row: k < bn the prefix state k (cascade; a prefix row past
+  // its tile's last row lives in the next tile's slots), then chunk k - bn.
+  const int nk = bn + n;
+  auto state_row = [&](int k) -> int64_t {
+    if (k >= bn) return (static_cast<int64_t>(sb) + k - bn) * R + r;
+    const int br = brow + r;
+    const int64_t s0 = static_cast<int64_t>(bsb) + k;
+    return br < a.base_rows ? s0 * a.base_rows + br
+                            : (s0 + a.base_tile_slots) * a.base_rows + br - a.base_rows;
+  };
+  auto ml_at = [&](int k) -> float2 {
+    return *reinterpret_cast<const float2*>((k < bn ? a.base_ml : a.part_ml) + 2 * state_row(k));
+  };
+  auto o_at = [&](int k) -> float2 {
+    return *reinterpret_cast<const float2*>((k < bn ? a.base_o : a.part_o) + state_row(k) * D +
+                                            2 * lane);
+  };
+  // This wave's states: k = k_first, k_first + k_step, ...
   const int k_first = WPR == 4 ? wave : 0;
   constexpr int k_step = WPR == 4 ? 4 : 1;
 
-  float2 v[kBatch];
-  float lk[kBatch];
+  float2 v[kBatch], mk[kBatch];
   auto load_batch = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int k = k0 + k_step * i;
-      if (k < n) {
-        const int64_t srow = static_cast<int64_t>(sb + k) * R + r;
-        lk[i] = a.part_lse[srow];
-        v[i] = *reinterpret_cast<const float2*>(a.part_o + srow * D + 2 * lane);
+      if (k < nk) {
+        mk[i] = ml_at(k);
+        v[i] = o_at(k);
       }
     }
   };
   load_batch(k_first);
 
-  const float* lse = a.part_lse + static_cast<int64_t>(sb) * R + r;   // chunk k at lse[k * R]
-  // Lane l holds the LSE of chunk l (the first 64 chunks) for both reductions.
-  const float l0 = lane < n ? lse[static_cast<int64_t>(lane) * R] : neg_inf();
-  float M = l0;
-  for (int k = lane + 64; k < n; k += 64) M = fmaxf(M, lse[static_cast<int64_t>(k) * R]);
-  M = wave_max(M);
+  // Lane l holds (m, l) of state l (the first 64 states) for both reductions.
+  const float2 ml0 = lane < nk ? ml_at(lane) : make_float2(neg_inf(), 0.f);
+  float M = ml0.x;
+  for (int k = lane + 64; k < nk; k += 64) M = fmaxf(M, ml_at(k).x);
+  M = wave_reduce_max(M);
   // An attention sink of the row's head is one more state (0, sink): it
   // enters the maximum and the sum, and adds nothing to the output.
-  const float sink = a.sinks != nullptr ? a.sinks[orow % a.num_qo_heads] : neg_inf();
+  const float sink = a.sinks != nullptr ? a.sinks[orow % a.num_qo_heads] * kLog2e : neg_inf();
   M = fmaxf(M, sink);
-  // A base state of the row (the cascade's prefix) enters like one more chunk,
-  // added after the chunks.
-  const float base = a.base_lse != nullptr ? a.base_lse[orow] : neg_inf();
-  M = fmaxf(M, base);
   const float Mu = (M == neg_inf()) ? 0.f : M;
-  float L = lane < n ? fast_exp2((l0 - Mu) * kLog2e) : 0.f;
-  for (int k = lane + 64; k < n; k += 64)
-    L += fast_exp2((lse[static_cast<int64_t>(k) * R] - Mu) * kLog2e);
-  L = wave_sum(L) + fast_exp2((sink - Mu) * kLog2e);
-  const float w_base = fast_exp2((base - Mu) * kLog2e);   // 0 without a base state
-  L += w_base;
+  float L = lane < nk ? ml0.y * fast_exp2(ml0.x - Mu) : 0.f;
+  for (int k = lane + 64; k < nk; k += 64) {
+    const float2 ml = ml_at(k);
+    L += ml.y * fast_exp2(ml.x - Mu);
+  }
+  L = wave_reduce_sum(L) + fast_exp2(sink - Mu);
 
   float o0 = 0.f, o1 = 0.f;
-  for (int k0 = k_first; k0 < n; k0 += k_step * kBatch) {
+  for (int k0 = k_first; k0 < nk; k0 += k_step * kBatch) {
     if (k0 != k_first) load_batch(k0);
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      if (k0 + k_step * i < n) {
-        const float w = fast_exp2((lk[i] - Mu) * kLog2e);
+      if (k0 + k_step * i < nk) {
+        const float w = mk[i].y * fast_exp2(mk[i].x - Mu);
         o0 += w * v[i].x;
         o1 += w * v[i].y;
       }
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
+  const float lse = L > 0.f ? (M + fast_log2(L)) * kLn2 : neg_inf();
   if constexpr (WPR == 4) {
     s_red[wave][2 * lane] = o0;
     s_red[wave][2 * lane + 1] = o1;
     __syncthreads();
     const int tid = threadIdx.x;
     if (tid < D) {
-      float sum = ((s_red[0][tid] + s_red[1][tid]) + s_red[2][tid]) + s_red[3][tid];
-      if (a.base_o != nullptr) sum += w_base * a.base_o[orow * D + tid];
+      const float sum = ((s_red[0][tid] + s_red[1][tid]) + s_red[2][tid]) + s_red[3][tid];
       store_f(static_cast<OUT*>(a.o) + orow * D + tid, sum * inv);
     }
-    if (tid == 0 && a.lse != nullptr) a.lse[orow] = L > 0.f ? M + __logf(L) : neg_inf();
+    if (tid == 0 && a.lse != nullptr) a.lse[orow] = lse;
   } else {
-    if (a.base_o != nullptr) {
-      const float2 bv = *reinterpret_cast<const float2*>(a.base_o + orow * D + 2 * lane);
-      o0 += w_base * bv.x;
-      o1 += w_base * bv.y;
-    }
     OUT* out = static_cast<OUT*>(a.o) + orow * D + 2 * lane;
     store_f(out, o0 * inv);
     store_f(out + 1, o1 * inv);
-    if (lane == 0 && a.lse != nullptr) a.lse[orow] = L > 0.f ? M + __logf(L) : neg_inf();
+    if (lane == 0 && a.lse != nullptr) a.lse[orow] = lse;
   }
 }
 

@@ -22,9 +22,12 @@ struct PlanItem {
 };
 static_assert(sizeof(PlanItem) == 32, "PlanItem is 8 int32");
 
-// A (request, tile, KV head) group whose KV range was split into chunks.
+// A (request, tile, KV head) group whose KV range was split into chunks (or
+// any group, with group_all). A cascade's suffix group also names the prefix
+// states its merge adds: base_num_chunks slots from base_slot_begin of the
+// prefix part, at row base_row of each (all 0 elsewhere).
 struct MergeGroup {
-  int32_t b, tile, g, slot_begin, num_chunks, pad0, pad1, pad2;
+  int32_t b, tile, g, slot_begin, num_chunks, base_slot_begin, base_num_chunks, base_row;
 };
 static_assert(sizeof(MergeGroup) == 32, "MergeGroup is 8 int32");
 

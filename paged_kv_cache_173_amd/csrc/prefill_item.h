@@ -718,8 +718,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
       }
     }
     const float inv = l_tot > 0.f ? o_scale / l_tot : 0.f;
-    const float lse = l_ex > 0.f ? (m_fin + fast_log2(l_ex)) * kLn2 : neg_inf();
     if (slot < 0) {
+      const float lse = l_ex > 0.f ? (m_fin + fast_log2(l_ex)) * kLn2 : neg_inf();
       const int64_t orow = static_cast<int64_t>(q0 + qtok[rb]) * a.num_qo_heads + head[rb];
       OUT* o = static_cast<OUT*>(a.o) + orow * D;
 #pragma unroll
@@ -743,7 +743,8 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
               f32x4{acc[rb][mb][4 * q4] * inv, acc[rb][mb][4 * q4 + 1] * inv,
                     acc[rb][mb][4 * q4 + 2] * inv, acc[rb][mb][4 * q4 + 3] * inv};
         }
-      if (half == 0) a.part_lse[srow_out] = lse;
+      // The chunk's (m, l): its exponent reference and the (unrounded) weight sum.
+      if (half == 0) *reinterpret_cast<f32x2*>(a.part_ml + 2 * srow_out) = f32x2{m_fin, l_ex};
     }
   }
 }

@@ -61,8 +61,9 @@ class pkv_variant(ctypes.Structure):
 class pkv_plan_part(ctypes.Structure):
     _fields_ = [("num_items", _I32), ("num_groups", _I32), ("chunk_pages", _I32),
                 ("rows_per_tile", _I32), ("num_slots", _I32), ("causal", _I32),
-                ("window_left", _I32), ("reserved", _I32), ("items_off", _I64), ("groups_off", _I64), ("kv_len_off", _I64),
-                ("part_o_off", _I64), ("part_lse_off", _I64)]
+                ("window_left", _I32), ("reserved", _I32), ("items_off", _I64),
+                ("groups_off", _I64), ("kv_len_off", _I64), ("part_o_off", _I64),
+                ("part_ml_off", _I64)]
 
 
 class pkv_plan_info(ctypes.Structure):
@@ -71,7 +72,7 @@ class pkv_plan_info(ctypes.Structure):
                 ("head_dim", _I32), ("page_size", _I32), ("total_qo", _I32),
                 ("sched", pkv_sched), ("int_ws", _P), ("float_ws", _P),
                 ("int_ws_required", _I64), ("float_ws_required", _I64),
-                ("cascade_state_off", _I64), ("order_off", _I64), ("num_blocks", _I32),
+                ("order_off", _I64), ("num_blocks", _I32),
                 ("batch2", _I32), ("part", pkv_plan_part * 2)]
 
 

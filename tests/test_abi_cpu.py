@@ -27,7 +27,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_struct_size(lib):
-    assert lib.pkv_abi_version() == 3
+    assert lib.pkv_abi_version() == 4
     assert lib.pkv_plan_info_size() == ctypes.sizeof(lib.pkv_plan_info)
 
 

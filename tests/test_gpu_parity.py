@@ -2,8 +2,8 @@
 
 Every case prints its name before it runs. Sizes: the reduced workloads span
 several tiles, several KV chunks and ragged tails; the full-size workloads run
-in the launch configuration the benchmark times and are compared on sampled
-requests the oracle computes one by one.
+in the launch configuration the benchmark times and are compared with the
+oracle on every row.
 """
 
 import numpy as np
@@ -55,21 +55,16 @@ def test_full_batch_decode(pkv, ws):
     _check(pkv, ws, wl.FULL[1](), "full[1] batch decode")
 
 
-def test_full_prefill_sampled(pkv, ws):
-    w = wl.FULL[2]()
-    qo = w.meta["qo_lens"]
-    sample = sorted({int(np.argmax(qo)), int(np.argmin(qo)), 5})
-    _check(pkv, ws, w, f"full[2] prefill requests {sample}", requests=sample)
+def test_full_prefill(pkv, ws):
+    _check(pkv, ws, wl.FULL[2](), "full[2] causal prefill, every row")
 
 
-def test_full_cascade_sampled(pkv, ws):
-    w = wl.FULL[3]()
-    _check(pkv, ws, w, "full[3] cascade requests 0,1,77,127", requests=[0, 1, 77, 127])
+def test_full_cascade(pkv, ws):
+    _check(pkv, ws, wl.FULL[3](), "full[3] cascade, every row")
 
 
-def test_full_long_decode_sampled(pkv, ws):
-    w = wl.FULL[4]()
-    _check(pkv, ws, w, "full[4] long decode request 2", requests=[2])
+def test_full_long_decode(pkv, ws):
+    _check(pkv, ws, wl.FULL[4](), "full[4] long decode, every row")
 
 
 # ----------------------------------------------------------------------------
@@ -220,3 +215,41 @@ def test_page_permutation_invariance(pkv, ws):
     w.kv.kv_indices = perm[w.kv.kv_indices]
     o2, l2 = run_gpu(pkv, Uploaded(w), ws)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ----------------------------------------------------------------------------
+# merges of split groups and the cascade's level-1 merge of prefix states
+# ----------------------------------------------------------------------------
+def test_cascade_rows_straddling_prefix_tiles(pkv, ws):
+    """G = 3 does not divide the 128-row level-0 tile: request 42's rows (packed rows
+    126..128) lie in two prefix tiles; the prefix is split into several chunks."""
+    sfx = list(np.random.default_rng(3).integers(0, 60, size=50))
+    w = wl.cascade(seed=420, batch=50, prefix_len=700, suffix_lens=sfx, num_qo_heads=6,
+                   num_kv_heads=2, page_size=16, canary=True)
+    _check(pkv, ws, w, "cascade G=3, 50 requests", sched=(256, 8, 16))
+
+
+def test_split_prefill_of_many_chunks(pkv, ws):
+    """Split prefill groups of 32+ chunks on average: the merge kernel's four-waves-per-row
+    mapping."""
+    w = wl.batch_prefill(seed=421, qo_lens=[100, 3], prefix_lens=[3000, 2500], num_qo_heads=8,
+                         num_kv_heads=2, page_size=16, dtype="bf16", canary=True)
+    sched = (1024, 16, 16)
+    _, groups, counts = pkv.pkv_plan_host(pkv.PKV_KIND_PREFILL, w.qo_indptr, w.kv.kv_indptr,
+                                          w.kv.last_page_len, 8, 2, 16, 1, sched)
+    assert counts[3] >= 32 * len(groups)
+    _check(pkv, ws, w, "prefill split into 32+ chunks per group", sched=sched)
+
+
+def test_split_merges_are_reproducible(pkv, ws):
+    """Split decode groups, the cascade (prefix chunk states merged with the suffix chunks)
+    and the single decode, run 20 times back to back: every run gives the same bits."""
+    cases = [(wl.SMALL[4](), (256, 16, 16)), (wl.SMALL[3](), (256, 16, 16)),
+             (wl.SMALL[0](), None)]
+    for w, sched in cases:
+        say(f"[case] repeated runs: {w.kind} sched={sched}")
+        up = Uploaded(w)
+        ref = run_gpu(pkv, up, ws, sched=sched)
+        for _ in range(19):
+            o, lse = run_gpu(pkv, up, ws, sched=sched)
+            assert np.array_equal(o, ref[0]) and np.array_equal(lse, ref[1], equal_nan=True)

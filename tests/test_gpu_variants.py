@@ -223,15 +223,13 @@ def test_prefill_all_variants(pkv, ws, dtype):
                     label=f"prefill window+cap+sinks {dtype} sched={sched}")
 
 
-def test_prefill_full_size_all_variants_sampled(pkv, ws):
+def test_prefill_full_size_all_variants(pkv, ws):
     """The full causal prefill workload (16 requests, 128..1024 new tokens after up to
     2048 cached, 32/8 heads, bf16) in the benchmark's launch configuration with window
-    1024, cap 50 and sinks; sampled requests, all heads."""
+    1024, cap 50 and sinks; every row against the oracle."""
     w = wl.FULL[2]()
-    qo = w.meta["qo_lens"]
-    sample = sorted({int(np.argmax(qo)), int(np.argmin(qo)), 5})
     run_prefill(pkv, ws, w, W=1024, cap=50.0, sinks=_sinks(450, 32, special=False),
-                requests=sample, label=f"full prefill requests {sample}, window+cap+sinks")
+                label="full prefill, window+cap+sinks, every row")
 
 
 def test_no_variant_matches_plain_path(pkv, ws):
@@ -252,9 +250,9 @@ def test_no_variant_matches_plain_path(pkv, ws):
 
 @pytest.mark.parametrize("regime", ["four_waves_per_row", "one_wave_per_row"])
 def test_decode_merge_of_many_chunks(pkv, ws, regime):
-    """Split groups of more than 64 chunks (the merge's LSE loops past one chunk per lane,
-    several batches of output loads) under both merge mappings: four waves sharing a row when
-    the groups average 32 chunks or more, one wave per row otherwise; with sinks."""
+    """Split decode groups of more than 64 chunks (the in-kernel merge's per-row loops
+    past one chunk per lane), with sinks: groups that average 32 chunks or more, and a plan
+    whose many one-chunk groups sit beside one long split group."""
     if regime == "four_waves_per_row":
         lens = [5000, 3100]
     else:
