@@ -400,6 +400,22 @@ pkv_status pkv_single_decode(const void* q, const void* k, const void* v, int32_
                              void* float_ws, size_t float_ws_bytes, int64_t* float_ws_required,
                              void* o, float* lse, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): as
+ * pkv_single_decode, with the partial states in a fixed 32 MiB device array
+ * that the library holds on each device it runs on until the process ends,
+ * instead of a caller workspace. The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine). Every call on a device shares that
+ * device's array: calls that overlap on one device race. The partial states
+ * take Hq * 520 B per chunk of the KV; the default sched makes at most about
+ * 2048 / Hkv chunks (under 18 MB for G <= 16). A kv_len / sched that needs
+ * more than 32 MiB is rejected with PKV_ERR_WORKSPACE_TOO_SMALL. Other errors
+ * as pkv_single_decode. */
+pkv_status pkv_single_decode_noalloc(const void* q, const void* k, const void* v, int32_t kv_len,
+                                     int32_t num_qo_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, pkv_dtype dtype, float sm_scale,
+                                     const pkv_sched* sched, void* o, float* lse, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Attention-state merges (docs index "Merge Attention States"). For each
  * row: s* = max_k s_k; w_k = exp(s_k - s*); O = sum w_k v_k / sum w_k;

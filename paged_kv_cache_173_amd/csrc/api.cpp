@@ -934,6 +934,68 @@ pkv_status pkv_single_decode(const void* q, const void* k, const void* v, int32_
   return ok();
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free single decode: the split partial states live in a fixed
+// device array of this library instead of a caller workspace. In host code
+// `scratch` names a host-side stand-in, not device memory: its device address
+// is taken once per device (hipGetSymbolAddress, that device current) and only
+// that address is passed to kernels. Every call on a device shares the array;
+// nothing in it needs to start at zero (each chunk writes its whole partial
+// state before the merge launch reads it), and calls that overlap on one
+// device race.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int64_t kScratchBytes = int64_t{32} << 20;
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device.
+pkv_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PKV_ERR_UNSUPPORTED, "device index above the library's limit of 64");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_single_decode_noalloc(const void* q, const void* k, const void* v, int32_t kv_len,
+                                     int32_t num_qo_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, pkv_dtype dtype, float sm_scale,
+                                     const pkv_sched* sched, void* o, float* lse, void* stream) {
+  void* ws = nullptr;
+  pkv_status st = scratch_of_current_device(&ws);
+  if (st) return st;
+  int64_t need = 0;
+  st = pkv_single_decode(q, k, v, kv_len, num_qo_heads, num_kv_heads, head_dim, dtype, sm_scale,
+                         sched, ws, static_cast<size_t>(kScratchBytes), &need, o, lse, stream);
+  if (st == PKV_ERR_WORKSPACE_TOO_SMALL)
+    return fail(PKV_ERR_WORKSPACE_TOO_SMALL,
+                "the partial states need " + std::to_string(need) +
+                    " B; the fixed scratch holds " + std::to_string(kScratchBytes) +
+                    " B (fewer chunks: a sched with a larger min_chunk_tokens or fewer slots)");
+  return st;
+}
+
 static pkv_status check_merge_args(int32_t n, int32_t num_heads, int32_t head_dim,
                                    pkv_dtype v_dtype) {
   if (n < 0 || num_heads <= 0 || head_dim <= 0)

@@ -121,6 +121,9 @@ _lib_prefill_run = _sig("pkv_prefill_run", _I32,
 _lib_single_decode = _sig("pkv_single_decode", _I32,
                           [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _F32,
                            ctypes.POINTER(pkv_sched), _P, _SZ, ctypes.POINTER(_I64), _P, _P, _P])
+_lib_single_decode_noalloc = _sig("pkv_single_decode_noalloc", _I32,
+                                  [_P, _P, _P, _I32, _I32, _I32, _I32, _I32, _F32,
+                                   ctypes.POINTER(pkv_sched), _P, _P, _P])
 _lib_merge_state = _sig("pkv_merge_state", _I32,
                         [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P])
 _lib_merge_state_in_place = _sig("pkv_merge_state_in_place", _I32,
@@ -463,6 +466,22 @@ def pkv_single_decode(q, k, v, sm_scale: float, float_ws=None, sched=None, o=Non
         st = _lib_single_decode(*args, float_ws.data_ptr(), need.value, ctypes.byref(need),
                                 o.data_ptr(), _ptr(lse), _stream(stream))
     _check(st, "pkv_single_decode")
+    return o, lse
+
+
+def pkv_single_decode_noalloc(q, k, v, sm_scale: float, sched=None, o=None, lse=None,
+                              stream=None):
+    """As pkv_single_decode, with the partial states in the library's fixed device scratch
+    (the call allocates no device memory; o / lse are allocated here only if not given)."""
+    q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+    if k.shape != v.shape or k.dim() != 3:
+        raise ValueError("k and v must both be [kv_len, num_kv_heads, head_dim]")
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty(q.shape[:1], dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(_lib_single_decode_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), k.shape[0],
+                                      q.shape[0], k.shape[1], k.shape[2], dtype_code(q.dtype),
+                                      float(sm_scale), _sched_arg(sched), o.data_ptr(),
+                                      _ptr(lse), _stream(stream)), "pkv_single_decode_noalloc")
     return o, lse
 
 
