@@ -1,27 +1,34 @@
 """Benchmark of the paged-KV attention hot path on one MI355X.
 
-Default workload: batch paged decode, GQA (64 requests, KV length uniform in
-[512, 4096], 32 query / 8 KV heads, head_dim 128, fp16, 16-token pages, pool
-1.25x the pages needed). A step is one run of the planned pass (decode
-kernel plus the merge of split chunks) over the whole batch; the host plan is
-made once per workload before timing and reused, as the plan/run split
-intends, and its host time is reported as plan_us (the median of 20 plan calls
-after warm-up, each on an idle stream; the call queues its table copy and
-returns without waiting for it).
+Default run: the five workloads of the build's contract, each timed, checked and set
+against its roofline, in one JSON line:
+  single  - single-request decode, kv_len 1024, 32/32 heads, fp16, contiguous KV;
+  decode  - batch paged decode, 64 requests, kv_len U[512, 4096], 32/8 heads, fp16,
+            16-token pages (the headline: `value` is its HBM throughput);
+  prefill - batch paged causal prefill, 16 requests, qo U[128, 1024] after a prefix
+            U[0, 2048], 32/8 heads, bf16;
+  cascade - 128 decode requests sharing an 8192-token prefix, suffix U[64, 1024], fp16;
+  long    - long-context split-KV decode, 4 x 131072 tokens, 64/8 heads, bf16, P = 64.
+A step is one run of the workload's planned pass (every kernel of it) over the whole
+batch; the host plan is made once before timing and reused, as the plan/run split
+intends, and its host time is reported as plan_us (median of 20 plan calls).
 
-Timing: W warm-up steps, then K timed steps. Before every step a 512 MiB
-buffer is read (outside the timed events) so the 256 MB Infinity Cache holds
-no KV and no dirty lines that would be written back during the step; each
-step is bracketed by HIP events on the stream the kernels run on.
-value = algorithmic bytes / mean step time. The attention kernel alone (the
-roofline figure) is timed in a second pass of K steps by a pair of events that
-its own dispatch carries (hipExtLaunchKernel), i.e. its begin and end
-timestamps, the same interval rocprofv3's kernel trace reports; those events
-lengthen a step by a few microseconds, so the step times come from the first
-pass, which carries none.
+Timing: W warm-up steps, then K timed steps. Before every step a 512 MiB buffer is read
+(outside the timed events) so the 256 MB Infinity Cache holds no KV and no dirty lines;
+each step is bracketed by HIP events on the stream the kernels run on, and the whole pass
+by a device synchronize. `value` and `ms_per_step` use the median step (the mean is
+reported beside it). The attention kernel alone (the roofline figure) is timed in a second
+pass of K steps by a pair of events its own dispatch carries (hipExtLaunchKernel), the
+interval rocprofv3's kernel trace reports; those events lengthen a step by a few
+microseconds, so step times come from the first pass.
 
-`--workload` selects another workload (single, decode, prefill, cascade,
-long); `--all` adds every workload's figures under "workloads" in the line.
+After timing, the output buffers of the last timed step are compared with the fp64
+oracle on every row (max |dO| and max |dLSE| in the line, against the tolerances), and
+the oracle is timed on the host cores on a bounded sample of the same workload
+(`cpu_baseline`). Neither touches the timed region.
+
+`--workload X` measures one workload (also append, block_sparse, pod, decode_variants,
+prefill_variants); `--all` adds those five to the default five.
 """
 
 from __future__ import annotations
@@ -340,7 +347,7 @@ class Runner:
 
 
 def time_steps(torch, runner, steps, warmup, flush):
-    """Returns (mean step ms, median step ms, mean attention-kernel ms or None, wall s).
+    """Returns (step ms list, attention-kernel ms list or None, wall s of the step pass).
 
     The K timed steps carry only the step's own pair of events. The attention kernel's
     time comes from a second pass of K steps in which the kernel's dispatch also carries
@@ -384,40 +391,141 @@ def time_steps(torch, runner, steps, warmup, flush):
             runner.step((k_begin[i], k_end[i]))
         torch.cuda.synchronize()
         kern = [b.elapsed_time(e) for b, e in zip(k_begin, k_end)]
-    return (float(np.mean(ms)), float(np.median(ms)),
-            float(np.mean(kern)) if kern else None, wall)
+    return ms, kern, wall
 
 
-def cpu_baseline(w, min_s=10.0, max_s=30.0):
-    """The oracle as it stands on the host cores: whole passes over the same batch, one
-    request at a time, until at least `min_s` seconds of CPU work (stopping early, mid-pass,
-    at `max_s`)."""
+# fp16: O <= 2e-3, LSE <= 1e-3; bf16: O <= 1e-2, LSE <= 2e-3 (max abs error against the oracle)
+TOL = {"f16": (2e-3, 1e-3), "bf16": (1e-2, 2e-3)}
+
+
+def _errors(o, lse, O, LSE):
+    """(max |dO|, max |dLSE| over rows the oracle gives a finite LSE, -inf rows agree)."""
+    o = np.asarray(o, np.float64)
+    lse = np.asarray(lse, np.float64)
+    inf_ref = np.isneginf(LSE)
+    agree = bool(np.array_equal(np.isneginf(lse), inf_ref)) and not np.isnan(o).any()
+    d_o = float(np.max(np.abs(o - O))) if o.size else 0.0
+    fin = ~inf_ref
+    d_l = float(np.max(np.abs(lse[fin] - LSE[fin]))) if fin.any() else 0.0
+    return d_o, d_l, agree
+
+
+def parity(runner):
+    """The output buffers of the last timed step against the fp64 oracle, on every row
+    (append: every byte of both page pools)."""
     import oracle
+    torch, w = runner.torch, runner.w
+
+    def host(t):
+        return t.float().cpu().numpy().astype(np.float64)
+
+    if torch.cuda.is_available():
+        torch.cuda.synchronize()
+    if w.kind == "append":
+        kv = w.kv
+        bi, pos = oracle.append_positions(w.append_indptr, kv.kv_indptr, kv.last_page_len,
+                                          kv.page_size)
+        K, V = oracle.append_paged_kv(kv.k_cache, kv.v_cache, w.append_k, w.append_v, bi, pos,
+                                      kv.kv_indptr, kv.kv_indices, kv.last_page_len)
+        same = (np.array_equal(runner.k.view(torch.int16).cpu().numpy().view(np.uint16), K) and
+                np.array_equal(runner.v.view(torch.int16).cpu().numpy().view(np.uint16), V))
+        return {"bit_exact": bool(same), "bytes_compared": int(K.nbytes + V.nbytes), "ok": same}
+    var = w.meta.get("variant", {}) if w.kind in ("decode", "prefill") else {}
+    win = int(var.get("window_left", -1))
+    cap = float(var.get("logits_soft_cap", 0.0))
+    sinks = var.get("sinks")
+    pairs = []
+    if w.kind == "pod":
+        wp, wd = w.prefill, w.decode
+        pairs.append((runner.o_p, runner.l_p, oracle.batch_prefill(
+            wp.q, wp.kv.k_cache, wp.kv.v_cache, wp.qo_indptr, wp.kv.kv_indptr,
+            wp.kv.kv_indices, wp.kv.last_page_len, wp.dtype, wp.sm_scale, wp.causal)))
+        pairs.append((runner.o_d, runner.l_d, oracle.batch_decode(
+            wd.q, wd.kv.k_cache, wd.kv.v_cache, wd.kv.kv_indptr, wd.kv.kv_indices,
+            wd.kv.last_page_len, wd.dtype, wd.sm_scale)))
+    elif w.kind == "single_decode":
+        pairs.append((runner.o, runner.lse, oracle.single_decode(w.q, w.k, w.v, w.dtype,
+                                                                 w.sm_scale)))
+    elif w.kind == "block_sparse":
+        pairs.append((runner.o, runner.lse, oracle.block_sparse_attention(
+            w.q, w.k, w.v, w.dtype, w.bsr_indptr, w.bsr_indices, w.row_block, w.col_block,
+            w.sm_scale)))
+    elif w.kind == "cascade":
+        kv = w.kv
+        pairs.append((runner.o, runner.lse, oracle.cascade_decode(
+            w.q, kv.k_cache, kv.v_cache, w.prefix_indices, w.prefix_last_page_len,
+            kv.kv_indptr, kv.kv_indices, kv.last_page_len, w.dtype, w.sm_scale)))
+    elif w.kind == "decode":
+        kv = w.kv
+        if win >= 0 or cap > 0 or sinks is not None:
+            ref = oracle.batch_decode_variant(w.q, kv.k_cache, kv.v_cache, kv.kv_indptr,
+                                              kv.kv_indices, kv.last_page_len, w.dtype,
+                                              w.sm_scale, win, cap, sinks)
+        else:
+            ref = oracle.batch_decode(w.q, kv.k_cache, kv.v_cache, kv.kv_indptr, kv.kv_indices,
+                                      kv.last_page_len, w.dtype, w.sm_scale)
+        pairs.append((runner.o, runner.lse, ref))
+    else:
+        kv = w.kv
+        if win >= 0 or cap > 0 or sinks is not None:
+            ref = oracle.batch_prefill_variant(w.q, kv.k_cache, kv.v_cache, w.qo_indptr,
+                                               kv.kv_indptr, kv.kv_indices, kv.last_page_len,
+                                               w.dtype, w.sm_scale, w.causal, win, cap, sinks)
+        else:
+            ref = oracle.batch_prefill(w.q, kv.k_cache, kv.v_cache, w.qo_indptr, kv.kv_indptr,
+                                       kv.kv_indices, kv.last_page_len, w.dtype, w.sm_scale,
+                                       w.causal)
+        pairs.append((runner.o, runner.lse, ref))
+    to, tl = TOL[w.dtype]
+    d_o = d_l = 0.0
+    agree = True
+    rows = 0
+    for o, lse, (O, LSE) in pairs:
+        e_o, e_l, a = _errors(host(o), lse.cpu().numpy(), O, LSE)
+        d_o, d_l, agree = max(d_o, e_o), max(d_l, e_l), agree and a
+        rows += int(np.prod(LSE.shape))
+    return {"max_abs_dO": d_o, "max_abs_dLSE": d_l, "tol_O": to, "tol_LSE": tl,
+            "rows": rows, "neg_inf_rows_agree": agree,
+            "ok": bool(agree and d_o <= to and d_l <= tl)}
+
+
+def roofline_of(name, runner, step_ms, kernel_ms):
+    """The workload's bound and its fraction: HBM bytes or MFMA flops per attention-kernel
+    time, or (the cascade) the combined floor of its prefix and suffix passes per step."""
+    nbytes, flops, _ = runner.work()
+    t_s = (kernel_ms if kernel_ms is not None else step_ms) * 1e-3
+    timed = "attention kernel (events on its dispatch)" if kernel_ms is not None else "step"
+    if name == "cascade":
+        w = runner.w
+        pre = w.meta["prefix_len"] * w.num_kv_heads * w.head_dim * 2 * 2
+        pre_flops = 4.0 * w.num_qo_heads * w.head_dim * len(w.kv.kv_lens) * w.meta["prefix_len"]
+        floor_us = (nbytes / (HBM_PEAK_GBS * 1e9) + pre_flops / (MFMA_PEAK_TFLOPS * 1e12)) * 1e6
+        return {"bound": "hbm+mfma", "achieved": floor_us / (step_ms * 1e3), "peak": 1.0,
+                "unit": "fraction of the combined floor (all KV bytes at 8 TB/s + the prefix "
+                        "pass's flops at 2.5 PFLOP/s)", "frac": floor_us / (step_ms * 1e3),
+                "floor_us": floor_us, "kernel_us": step_ms * 1e3, "timed": "step",
+                "prefix_bytes": pre, "traffic": None}
+    if name in PREFILL_LIKE:
+        a = flops / t_s / 1e12
+        return {"bound": "mfma", "achieved": a, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": a / MFMA_PEAK_TFLOPS, "traffic": None, "kernel_us": t_s * 1e6,
+                "timed": timed}
+    a = nbytes / t_s / 1e9
+    return {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": a / HBM_PEAK_GBS, "traffic": profiled_traffic() if name == "decode" else None,
+            "kernel_us": t_s * 1e6, "timed": timed}
+
+
+def host_threads():
+    """(threads the oracle's BLAS uses, CPUs this process may run on). The BLAS thread
+    count follows OMP_NUM_THREADS where the environment sets it."""
+    cpus = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        cores = 1
-    kv = w.kv
-    t0 = time.perf_counter()
-    done = []
-    passes = 0
-    while time.perf_counter() - t0 < min_s:
-        for b in range(len(kv.kv_lens)):
-            oracle.batch_decode(w.q, kv.k_cache, kv.v_cache, kv.kv_indptr, kv.kv_indices,
-                                kv.last_page_len, w.dtype, w.sm_scale, requests=[b])
-            done.append(b)
-            if time.perf_counter() - t0 > max_s:
-                break
-        passes += 1
-        if time.perf_counter() - t0 > max_s:
-            break
-    dt = time.perf_counter() - t0
-    nbytes = decode_bytes(kv.kv_lens[done], w.num_kv_heads, w.head_dim, 2, len(done),
-                          w.num_qo_heads)
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"fp64 NumPy oracle, {len(done)} request evaluations ({passes} pass(es) over "
-                      f"the {len(kv.kv_lens)} requests of the same batch, all heads) in {dt:.1f} s"}
+        blas = 1
+    return int(blas), int(cpus)
 
 
 def oracle_units(runner):
@@ -509,11 +617,7 @@ def oracle_timing(runner, prefill_like, min_s=3.0, max_s=10.0):
     """The oracle on the host cores over a bounded sample of one step's work (whole units in
     order: at least one pass and `min_s` seconds, stopping once past `max_s`), in the
     workload's roofline unit."""
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = 1
+    cores, cpus = host_threads()
     nbytes, flops, _ = runner.work()
     units = oracle_units(runner)
     t0 = time.perf_counter()
@@ -531,9 +635,10 @@ def oracle_timing(runner, prefill_like, min_s=3.0, max_s=10.0):
     dt = time.perf_counter() - t0
     work = (flops if prefill_like else nbytes) * share
     return {"value": work / dt / (1e12 if prefill_like else 1e9),
-            "unit": "TFLOP/s" if prefill_like else "GB/s", "cores": int(cores), "kind": "oracle",
+            "unit": "TFLOP/s" if prefill_like else "GB/s", "cores": cores,
+            "affinity_cpus": cpus, "kind": "oracle",
             "sample": f"fp64 NumPy oracle, {n} unit evaluations ({len(units)} units make one "
-                      f"step; {share:.3f} steps' work) in {dt:.1f} s"}
+                      f"step; {share:.3f} steps' work) in {dt:.1f} s, {cores} BLAS threads"}
 
 
 # workloads whose roofline is the MFMA peak (the rest are bound by HBM)
@@ -565,16 +670,84 @@ def make_workload(name, wl):
     return wl.FULL[WORKLOADS[name]]()
 
 
+DEFAULT_FIVE = ("single", "decode", "prefill", "cascade", "long")
+EXTRA = ("append", "block_sparse", "pod", "decode_variants", "prefill_variants")
+
+DESCRIPTION = {
+    "single": "single-request decode, kv_len 1024, 32/32 heads, fp16, contiguous",
+    "decode": "batch paged decode, 64 requests, kv_len U[512,4096], 32/8 heads, P=16, fp16",
+    "prefill": "batch paged causal prefill, 16 requests, qo U[128,1024] after prefix "
+               "U[0,2048], 32/8 heads, P=16, bf16",
+    "cascade": "cascade, 128 requests, 8192-token shared prefix, suffix U[64,1024], "
+               "32/8 heads, P=16, fp16",
+    "long": "long-context split-KV decode, 4 x 131072 tokens, 64/8 heads, P=64, bf16",
+    "append": "append of the prefill workload's 10420 new tokens' K/V into the paged "
+              "cache, 8 KV heads, P=16, bf16",
+    "block_sparse": "block-sparse attention, 8192 x 8192 tokens, 64 x 64 blocks, "
+                    "density 0.25 + diagonal, 32/8 heads, bf16",
+    "pod": "mixed batch in one launch: the causal prefill workload's 16 requests and "
+           "64 decode requests with kv_len U[512,4096], 32/8 heads, P=16, bf16",
+    "decode_variants": "batch paged decode, 64 requests, kv_len U[512,4096], 32/8 heads, "
+                       "P=16, fp16, sliding window 1023, logit soft cap 30, sinks",
+    "prefill_variants": "batch paged causal prefill, 16 requests, qo U[128,1024] after "
+                        "prefix U[0,2048], 32/8 heads, P=16, bf16, sliding window 1023, "
+                        "logit soft cap 50, sinks",
+}
+
+
+def measure(name, wl, pkv, torch, args, flush, headline):
+    """Times one workload, checks its timed outputs against the oracle, sets it against its
+    roofline and times the oracle on a bounded sample; returns (result dict, runner)."""
+    t0 = time.perf_counter()
+    w = make_workload(name, wl)
+    r = Runner(name, w, pkv, torch)
+    log(f"[bench] {name}: generated and planned in {time.perf_counter() - t0:.1f} s "
+        f"(plan {r.plan_us:.0f} us); timing {args.steps} steps")
+    ms, kern, wall = time_steps(torch, r, args.steps, args.warmup, flush)
+    med, mean = float(np.median(ms)), float(np.mean(ms))
+    kern_med = float(np.median(kern)) if kern else None
+    nbytes, flops, tokens = r.work()
+    prefill_like = name in PREFILL_LIKE
+    res = {"config": DESCRIPTION[name], "ms_per_step": med, "ms_per_step_mean": mean,
+           "attention_kernel_ms": kern_med, "plan_us": r.plan_us,
+           "value": flops / (med * 1e-3) / 1e12 if prefill_like else nbytes / (med * 1e-3) / 1e9,
+           "unit": "TFLOP/s" if prefill_like else "GB/s",
+           "tokens_per_s": tokens / (med * 1e-3), "bytes": nbytes, "flops": flops,
+           "timed_pass_wall_s": wall}
+    res["roofline"] = roofline_of(name, r, med, kern_med)
+    if name == "pod":
+        # the same two parts as separate prefill and decode runs, timed the same way
+        r.sequential = True
+        s_ms, _, _ = time_steps(torch, r, args.steps, args.warmup, flush)
+        r.sequential = False
+        res["sequential_ms_per_step"] = float(np.median(s_ms))
+        res["pod_speedup"] = res["sequential_ms_per_step"] / med
+        r.step()                       # the outputs checked below are the mixed launch's
+    log(f"[bench] {name}: {med * 1e3:.1f} us/step (mean {mean * 1e3:.1f}), {res['value']:.4g} "
+        f"{res['unit']}; roofline {res['roofline']['bound']} frac {res['roofline']['frac']:.3f}")
+    if not args.no_parity:
+        t1 = time.perf_counter()
+        res["parity"] = parity(r)
+        log(f"[bench] {name}: parity {res['parity']} ({time.perf_counter() - t1:.1f} s)")
+    if not args.no_cpu_baseline:
+        lo, hi = (10.0, 30.0) if headline else (3.0, 8.0)
+        res["cpu_baseline"] = oracle_timing(r, prefill_like, min_s=lo, max_s=hi)
+        log(f"[bench] {name}: oracle {res['cpu_baseline']['value']:.4g} "
+            f"{res['cpu_baseline']['unit']} ({res['cpu_baseline']['sample']})")
+    return res, r
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
-    ap.add_argument("--all", action="store_true", help="also measure the other workloads")
+    ap.add_argument("--workload", default=None, choices=sorted(WORKLOADS),
+                    help="measure this workload alone (default: the five contract workloads)")
+    ap.add_argument("--all", action="store_true", help="also measure the extra workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-baselines", action="store_true",
-                    help="also time the oracle on a bounded sample of every measured workload")
+    ap.add_argument("--no-parity", action="store_true",
+                    help="skip the oracle check of the timed outputs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -586,104 +759,45 @@ def main():
     from paged_kv_cache_173_amd import pkv
     from paged_kv_cache_173_amd import workloads as wl
 
-    log(f"[bench] generating workload {args.workload}")
     flush = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
-    names = [args.workload] + ([n for n in ("single", "decode", "prefill", "cascade", "long",
-                                            "append", "block_sparse", "pod", "decode_variants",
-                                            "prefill_variants")
-                                 if n != args.workload] if args.all else [])
+    if args.workload is not None:
+        names = [args.workload]
+    else:
+        names = list(DEFAULT_FIVE) + (list(EXTRA) if args.all else [])
+    head_name = "decode" if "decode" in names else names[0]
     results = {}
-    headline = None
+    head_runner = None
     for name in names:
-        w = make_workload(name, wl)
-        r = Runner(name, w, pkv, torch)
-        log(f"[bench] {name}: planned in {r.plan_us:.0f} us; timing {args.steps} steps")
-        mean_ms, med_ms, kern_ms, wall = time_steps(torch, r, args.steps, args.warmup, flush)
-        nbytes, flops, tokens = r.work()
-        res = {"ms_per_step": mean_ms, "median_ms": med_ms, "attention_kernel_ms": kern_ms,
-               "plan_us": r.plan_us,
-               "GBps": nbytes / (mean_ms * 1e-3) / 1e9, "TFLOPs": flops / (mean_ms * 1e-3) / 1e12,
-               "tokens_per_s": tokens / (mean_ms * 1e-3), "bytes": nbytes, "flops": flops,
-               "wall_s": wall}
-        res["hbm_frac"] = res["GBps"] / HBM_PEAK_GBS
-        res["mfma_frac"] = res["TFLOPs"] / MFMA_PEAK_TFLOPS
-        kern_ms = kern_ms if kern_ms else mean_ms
-        res["kernel_GBps"] = nbytes / (kern_ms * 1e-3) / 1e9
-        res["kernel_TFLOPs"] = flops / (kern_ms * 1e-3) / 1e12
-        if name == "pod":
-            # the same two parts as separate prefill and decode runs, timed the same way
-            r.sequential = True
-            s_mean, s_med, s_kern, _ = time_steps(torch, r, args.steps, args.warmup, flush)
-            r.sequential = False
-            res["sequential_ms_per_step"] = s_mean
-            res["pod_speedup"] = s_mean / mean_ms
-            log(f"[bench] pod: separate prefill + decode runs {s_mean * 1e3:.1f} us/step; "
-                f"one mixed launch {mean_ms * 1e3:.1f} us/step ({s_mean / mean_ms:.3f}x)")
-        log(f"[bench] {name}: {mean_ms * 1e3:.1f} us/step, {res['GBps']:.0f} GB/s "
-            f"({100 * res['hbm_frac']:.1f}% HBM), {res['TFLOPs']:.1f} TFLOP/s; attention kernel "
-            f"{kern_ms * 1e3:.1f} us: {res['kernel_GBps']:.0f} GB/s, "
-            f"{res['kernel_TFLOPs']:.1f} TFLOP/s")
-        if args.cpu_baselines:
-            log(f"[bench] {name}: timing the CPU oracle on a bounded sample")
-            res["cpu_baseline"] = oracle_timing(r, name in PREFILL_LIKE)
-            log(f"[bench] {name}: oracle {res['cpu_baseline']['value']:.4g} "
-                f"{res['cpu_baseline']['unit']} ({res['cpu_baseline']['sample']})")
+        res, r = measure(name, wl, pkv, torch, args, flush, headline=name == head_name)
         results[name] = res
-        if headline is None:
-            headline = (name, w, r, res)
+        if name == head_name:
+            head_runner = r
         else:
             del r
-            torch.cuda.empty_cache()
+        torch.cuda.empty_cache()
 
-    name, w, r, res = headline
-    prefill_like = name in PREFILL_LIKE
+    res = results[head_name]
+    w = head_runner.w
+    prefill_like = head_name in PREFILL_LIKE
     line = {
         "metric": "paged decode HBM GB/s (% peak); prefill TFLOPS (% MFMA peak); tokens/s",
-        "value": res["TFLOPs"] if prefill_like else res["GBps"],
-        "unit": "TFLOP/s" if prefill_like else "GB/s",
+        "value": res["value"], "unit": res["unit"],
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None,
+        "ms_per_step": res["ms_per_step"], "ms_per_step_mean": res["ms_per_step_mean"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f16",
         "data": "synthetic",
-        "config": {"workload": {
-            "single": "single-request decode, kv_len 1024, 32/32 heads, fp16, contiguous",
-            "decode": "batch paged decode, 64 requests, kv_len U[512,4096], 32/8 heads, P=16, fp16",
-            "prefill": "batch paged causal prefill, 16 requests, qo U[128,1024] after prefix "
-                       "U[0,2048], 32/8 heads, P=16, bf16",
-            "cascade": "cascade, 128 requests, 8192-token shared prefix, suffix U[64,1024], "
-                       "32/8 heads, P=16, fp16",
-            "long": "long-context split-KV decode, 4 x 131072 tokens, 64/8 heads, P=64, bf16",
-            "append": "append of the prefill workload's 10420 new tokens' K/V into the paged "
-                      "cache, 8 KV heads, P=16, bf16",
-            "block_sparse": "block-sparse attention, 8192 x 8192 tokens, 64 x 64 blocks, "
-                            "density 0.25 + diagonal, 32/8 heads, bf16",
-            "pod": "mixed batch in one launch: the causal prefill workload's 16 requests and "
-                   "64 decode requests with kv_len U[512,4096], 32/8 heads, P=16, bf16",
-            "decode_variants": "batch paged decode, 64 requests, kv_len U[512,4096], 32/8 heads, "
-                               "P=16, fp16, sliding window 1023, logit soft cap 30, sinks",
-            "prefill_variants": "batch paged causal prefill, 16 requests, qo U[128,1024] after "
-                                "prefix U[0,2048], 32/8 heads, P=16, bf16, sliding window 1023, "
-                                "logit soft cap 50, sinks",
-        }[name], "head_dim": 128, "tokens_per_step": r.work()[2],
-            "tokens_per_s": res["tokens_per_s"], "plan_us": res["plan_us"]},
-        # the dominant kernel (the attention kernel, timed by the events its dispatch carries)
-        "roofline": {
-            "bound": "mfma" if prefill_like else "hbm",
-            "achieved": res["kernel_TFLOPs"] if prefill_like else res["kernel_GBps"],
-            "peak": MFMA_PEAK_TFLOPS if prefill_like else HBM_PEAK_GBS,
-            "unit": "TFLOP/s" if prefill_like else "GB/s",
-            "frac": (res["kernel_TFLOPs"] / MFMA_PEAK_TFLOPS) if prefill_like
-            else (res["kernel_GBps"] / HBM_PEAK_GBS),
-            "traffic": profiled_traffic() if name == "decode" else None,
-            "kernel_us": (res["attention_kernel_ms"] or res["ms_per_step"]) * 1e3,
-        },
+        "config": {"workload": DESCRIPTION[head_name], "head_dim": 128,
+                   "tokens_per_step": head_runner.work()[2],
+                   "tokens_per_s": res["tokens_per_s"], "plan_us": res["plan_us"]},
+        "roofline": res["roofline"],
     }
+    if "parity" in res:
+        line["parity"] = res["parity"]
+    if "cpu_baseline" in res:
+        line["cpu_baseline"] = res["cpu_baseline"]
     if len(results) > 1:
         line["workloads"] = results
-    if not args.no_cpu_baseline and name == "decode":
-        log("[bench] timing the CPU oracle on a bounded sample")
-        line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
 
 

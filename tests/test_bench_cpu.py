@@ -56,3 +56,31 @@ def test_oracle_units_cover_one_step(name):
     assert res["value"] > 0 and np.isfinite(res["value"])
     assert res["unit"] == ("TFLOP/s" if name in bench.PREFILL_LIKE else "GB/s")
     assert res["kind"] == "oracle"
+
+
+class _Outputs:
+    """A runner whose 'timed outputs' are given host tensors (the parity check's inputs)."""
+
+    def __init__(self, w, o, lse):
+        import torch
+        self.torch, self.w = torch, w
+        self.o, self.lse = torch.from_numpy(o), torch.from_numpy(lse)
+
+
+def test_parity_check_measures_errors_and_masked_rows():
+    import oracle
+    w = wl.batch_prefill(seed=11, qo_lens=[5, 40], prefix_lens=[0, 3], num_qo_heads=4,
+                         num_kv_heads=2, page_size=16, dtype="bf16")
+    kv = w.kv
+    O, LSE = oracle.batch_prefill(w.q, kv.k_cache, kv.v_cache, w.qo_indptr, kv.kv_indptr,
+                                  kv.kv_indices, kv.last_page_len, w.dtype, w.sm_scale, True)
+    res = bench.parity(_Outputs(w, O.copy(), LSE.copy()))
+    assert res["ok"] and res["max_abs_dO"] < 1e-6 and res["max_abs_dLSE"] < 1e-4   # fp32 round trip
+    assert res["rows"] == LSE.size
+    o = O.copy()
+    o[3, 1, 7] += 0.02                            # beyond the bf16 tolerance of 1e-2
+    res = bench.parity(_Outputs(w, o, LSE.copy()))
+    assert not res["ok"] and abs(res["max_abs_dO"] - 0.02) < 1e-6
+    lse = LSE.copy()
+    lse[0, 0] = -np.inf                           # a row the oracle says sees keys
+    assert not bench.parity(_Outputs(w, O.copy(), lse))["neg_inf_rows_agree"]
