@@ -35,28 +35,44 @@ def common_flags() -> list[str]:
             "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + common_flags() + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+# The debug variant: the prefill kernels fill their LDS tile buffers with NaN
+# before each item (PKV_DEBUG_LDS_POISON), for the tests of the counted waits.
+DEBUG_LIB_PATH = os.path.join(HERE, "libpkv_debug.so")
+DEBUG_DEFINES = ["-DPKV_DEBUG_LDS_POISON"]
+
+
+def _compile(job) -> str:
+    src, build_dir, defines = job
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc()] + common_flags() + defines + ["-x", "hip", "-c", os.path.join(CSRC, src),
+                                                  "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libpkv.so; returns the library path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as pool:
-        objs = list(pool.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path):
+    tmp = path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libpkv.so (and its debug variant
+    libpkv_debug.so); returns the library path."""
+    debug_dir = os.path.join(BUILD_DIR, "debug")
+    os.makedirs(debug_dir, exist_ok=True)
+    jobs = [(s, BUILD_DIR, []) for s in SOURCES] + [(s, debug_dir, DEBUG_DEFINES) for s in SOURCES]
+    with ThreadPoolExecutor(max_workers=8) as pool:
+        objs = list(pool.map(_compile, jobs))
+    _link(objs[:len(SOURCES)], LIB_PATH)
+    _link(objs[len(SOURCES):], DEBUG_LIB_PATH)
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {LIB_PATH} and {DEBUG_LIB_PATH}")
     return LIB_PATH
 
 

@@ -179,6 +179,19 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 31, half = lane >> 5;
   const int G = a.group;
+#ifdef PKV_DEBUG_LDS_POISON
+  // Debug builds: every LDS tile buffer starts as NaN (0xFFFF is a NaN in fp16
+  // and bf16), so a tile read before its load has landed poisons the output
+  // instead of reading rows left by an earlier item.
+  {
+    char* const bufs[8] = {sK0, sK1, sK2, sK3, sV0, sV1, sV2, sV3};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      for (int off = 16 * tid; off < kTileBytes; off += 16 * blockDim.x)
+        *reinterpret_cast<u32x4*>(bufs[i] + off) = u32x4{~0u, ~0u, ~0u, ~0u};
+    __syncthreads();
+  }
+#endif
 
   // The item's fields and the request's table entries are the same for every
   // lane; saying so keeps them (and the descriptors built from them) in SGPRs

@@ -17,7 +17,9 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpkv.so")
+# PKV_LIBRARY=libpkv_debug.so selects the debug build (LDS tiles NaN-filled
+# before each prefill item); the default is the product library.
+LIB_PATH = os.path.join(_HERE, os.environ.get("PKV_LIBRARY", "libpkv.so"))
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with paged_kv_cache_173_amd.build.build()")
