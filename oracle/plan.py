@@ -36,6 +36,20 @@ Rule (all integer arithmetic; ceil(a / b) for b > 0):
     listed, in the same order, as merge groups.
 5.  Items are executed longest first: sorted by descending KV token count,
     ties broken by ascending (b, tile, g, j).
+6.  ``group_all``: every group writes partial states and is a merge group, also
+    a group of one chunk (slots and merge groups as in 4, for every group). The
+    cascade plans both of its levels this way (``cascade_spec``).
+
+The cascade (docs index "Cascade Attention": a shared prefix evaluated once,
+then merged with each request's suffix; article "FlashInfer", section
+"Attention states") is planned as two parts. Level 0 is one "request" whose
+query tokens are the batch's decode tokens (Q = batch) over the prefix
+(L = prefix length), unmasked, 128-row tiles; level 1 is the batch decode over
+the suffixes. Both with ``group_all``. Suffix group (b, g) also merges the
+level-0 states of its G rows: packed rows b*G .. b*G + G - 1 of KV head g at
+level 0, i.e. tile t = (b*G) // 128 from row (b*G) % 128 on (rows past 127 are
+the next tile's first rows), whose n0 chunk slots start at (t * Hkv + g) * n0
+(n0: the chunks of every level-0 group, which all have the same extent).
 """
 
 from __future__ import annotations
@@ -60,7 +74,7 @@ class PlanSpec:
 
 def plan_spec(qo_lens, kv_lens, page_size: int, num_kv_heads: int, group_size: int,
               rows_per_tile: int, causal: bool, num_cus: int, wg_per_cu: int,
-              min_chunk_tokens: int, window_left: int = -1) -> PlanSpec:
+              min_chunk_tokens: int, window_left: int = -1, group_all: bool = False) -> PlanSpec:
     """Apply the rule in the module docstring. ``qo_lens`` / ``kv_lens`` per request."""
     P, G = int(page_size), int(group_size)
     B = len(kv_lens)
@@ -86,20 +100,39 @@ def plan_spec(qo_lens, kv_lens, page_size: int, num_kv_heads: int, group_size: i
     slot = 0
     for (b, tile, kv_end, p_lo, pages) in tiles:     # (b, tile) order
         n_chunks = max(1, _ceil_div(pages, c))
+        grouped = n_chunks > 1 or group_all
         for g in range(num_kv_heads):                # then g
-            slot_begin = slot if n_chunks > 1 else -1
-            if n_chunks > 1:
+            slot_begin = slot if grouped else -1
+            if grouped:
                 spec.merge_groups.append((b, tile, g, slot_begin, n_chunks))
                 slot += n_chunks
             for j in range(n_chunks):
                 p0, p1 = p_lo + j * c, p_lo + min((j + 1) * c, pages)
                 k0, k1 = min(p0 * P, kv_end), min((p_lo + (j + 1) * c) * P, kv_end)
-                item = (b, g, tile, p0, p1, k0, k1, slot_begin + j if n_chunks > 1 else -1)
+                item = (b, g, tile, p0, p1, k0, k1, slot_begin + j if grouped else -1)
                 raw.append((k1 - k0, b, tile, g, j, item))
     raw.sort(key=lambda r: (-r[0], r[1], r[2], r[3], r[4]))
     spec.items = [r[5] for r in raw]
     spec.num_slots = slot
     return spec
+
+
+def cascade_spec(prefix_len: int, suffix_lens, page_size: int, num_kv_heads: int,
+                 group_size: int, sched_prefix, sched_suffix):
+    """(level-0 PlanSpec, level-1 PlanSpec, base) of the cascade rule in the module
+    docstring; base[i] = (base_slot_begin, base_num_chunks, base_row) of the i-th
+    level-1 merge group. ``sched_*`` = (num_cus, wg_per_cu, min_chunk_tokens)."""
+    B, G, H = len(suffix_lens), int(group_size), int(num_kv_heads)
+    level0 = plan_spec([B], [prefix_len], page_size, H, G, 128, False, *sched_prefix,
+                       group_all=True)
+    level1 = plan_spec([1] * B, list(suffix_lens), page_size, H, G, G, False, *sched_suffix,
+                       group_all=True)
+    n0 = level0.merge_groups[0][4] if level0.merge_groups else 0
+    base = []
+    for (b, _tile, g, _sb, _n) in level1.merge_groups:
+        t = (b * G) // 128
+        base.append(((t * H + g) * n0, n0, (b * G) % 128))
+    return level0, level1, base
 
 
 def pod_order(items_a, items_b) -> list:

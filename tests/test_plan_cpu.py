@@ -274,3 +274,23 @@ def test_long_item_cases_reach_three_radix_digits():
         rng = np.random.default_rng(4100 + seed)
         longest = max(longest, int(np.exp2(rng.uniform(0, 24, size=24)).max()))
     assert longest >= 1 << 22
+
+
+def test_group_all_changes_only_the_slots():
+    """With group_all every group gets partial slots and a merge record; the chunks
+    (items' page and token ranges, their order) are those of the plain rule, and a
+    brute-force count gives one slot per chunk."""
+    rng = np.random.default_rng(71)
+    for _ in range(50):
+        B = int(rng.integers(0, 6))
+        qo = rng.integers(1, 40, size=B)
+        kv = qo + rng.integers(0, 300, size=B)
+        args = (qo, kv, int(rng.choice([1, 16])), int(rng.integers(1, 4)), 4, 128,
+                bool(rng.integers(0, 2)), 64, int(rng.integers(1, 8)), 16)
+        plain, every = plan_spec(*args), plan_spec(*args, group_all=True)
+        assert [it[:7] for it in plain.items] == [it[:7] for it in every.items]
+        assert all(it[7] >= 0 for it in every.items)
+        assert every.num_slots == len(every.items)
+        assert len(every.merge_groups) == sum(1 for _ in {(it[0], it[2], it[1]) for it in every.items})
+        split = {(g[0], g[1], g[2]) for g in plain.merge_groups}
+        assert split <= {(g[0], g[1], g[2]) for g in every.merge_groups}

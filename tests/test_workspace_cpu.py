@@ -156,3 +156,51 @@ def test_plan_export_equals_the_host_rule(lib, kind_name):
             assert st == lib.PKV_ERR_WORKSPACE_TOO_SMALL
         st = lib._lib_plan_export(ctypes.byref(info), host.ctypes.data, 1, None, 0, None, 0)
         assert st == lib.PKV_ERR_INVALID_ARG         # one-part plans have no part 1
+
+
+def test_cascade_plan_export_equals_the_rule(lib):
+    """The cascade's two parts, exported from its plan, equal the oracle's cascade rule item
+    for item: level 0 (the prefix, every group writing chunk states) and level 1 (the
+    suffix decode, every (request, KV head) group a merge group), including the prefix
+    states (slots, count, first row) each level-1 group merges."""
+    from oracle.plan import cascade_spec
+    rng = np.random.default_rng(897)
+    for trial in range(30):
+        sched = SCHEDS[trial % len(SCHEDS)]
+        P = int(rng.choice([1, 5, 16, 32]))
+        Hkv = int(rng.choice([1, 2, 8]))
+        G = int(rng.choice([1, 3, 4, 16]))
+        Hq = Hkv * G
+        B = int(rng.integers(1, 60))
+        pre_pages = int(rng.integers(0, 40))
+        pre_lpl = int(rng.integers(1, P + 1)) if pre_pages else 0
+        pre_len = (pre_pages - 1) * P + pre_lpl if pre_pages else 0
+        sfx = rng.integers(0, 200, size=B)
+        ip, lpl = lens_to_table(rng, sfx, P)
+        s = lib.pkv_sched(*sched)
+
+        def call(host, info):
+            return lib._lib_cascade_plan(pre_pages, pre_lpl, lib._i32p(ip), lib._i32p(lpl), B,
+                                         Hq, Hkv, 128, P, 0, ctypes.byref(s), None, 0, None, 0,
+                                         host.ctypes.data, host.nbytes, None, ctypes.byref(info))
+        st, info, _ = plan_header(lib, call, 0)
+        st, info, host = plan_header(lib, call, int(info.int_ws_required))
+        assert st in (lib.PKV_OK, lib.PKV_ERR_WORKSPACE_TOO_SMALL)
+        level0, level1, base = cascade_spec(pre_len, sfx, P, Hkv, G, sched, sched)
+        for part, spec in ((0, level0), (1, level1)):
+            p = info.part[part]
+            assert p.num_items == len(spec.items) and p.num_groups == len(spec.merge_groups)
+            items = np.zeros((max(1, p.num_items), 8), np.int32)
+            groups = np.zeros((max(1, p.num_groups), 8), np.int32)
+            st = lib._lib_plan_export(ctypes.byref(info), host.ctypes.data, part,
+                                      lib._i32p(items), p.num_items, lib._i32p(groups),
+                                      p.num_groups)
+            assert st == lib.PKV_OK
+            assert [tuple(r) for r in items[:p.num_items].tolist()] == spec.items, (trial, part)
+            assert [tuple(r[:5]) for r in groups[:p.num_groups].tolist()] == spec.merge_groups
+            if part == 1:
+                assert [tuple(r[5:]) for r in groups[:p.num_groups].tolist()] == base, trial
+                # one group per (request, KV head), consecutive slots
+                assert len(spec.merge_groups) == B * Hkv
+                sb = [g[3] for g in spec.merge_groups]
+                assert sb == sorted(sb) and sb[0] == 0
