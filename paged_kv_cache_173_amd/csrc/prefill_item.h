@@ -13,19 +13,23 @@
 // "flashinfer.prefill", "KV-Cache Layout in FlashInfer").
 //
 // How it maps to CDNA4:
-//   * Workgroup = 4 waves, wave w owns rows 32w .. 32w+31 of the tile; a row
-//     is (query token, query head) with the G heads of a KV group packed
+//   * Workgroup = 4 waves, wave w owns rows 32w .. 32w+31 of the 128-row tile;
+//     a row is (query token, query head) with the G heads of a KV group packed
 //     together, so each K/V tile read from HBM serves G heads.
-//   * KV advances in 64-token tiles, double-buffered in LDS. The tiles go
-//     from HBM straight into LDS (buffer / global loads with the LDS flag), so
-//     no registers hold them in flight and no instructions copy them: wave w
-//     fetches the 16-token group w of the next tile (four 1 KB loads for K,
-//     four for V) while every wave computes the current one. The page id of a
-//     group is read one tile before its loads are issued. With page_size a
-//     multiple of 16 a group lies in one page: one descriptor per wave and
-//     tile, ranged to the group's valid tokens so that tokens past the item
-//     read as zero; other page sizes look up every token and repeat the last
-//     valid one past the end (its weight is exactly 0).
+//   * KV advances in 32-token tiles (KT) through a four-deep LDS ring per
+//     operand (sK0..sK3, sV0..sV3, 8 KB each, 64 KB per workgroup): K is
+//     loaded four tiles ahead, V three. Tiles go from HBM straight into LDS
+//     (buffer / global loads with the LDS flag), so no registers hold them in
+//     flight and no instructions copy them: wave w fetches kRpw = KT / NW = 8
+//     token rows of each tile (two 1 KB loads for K, two for V). Each
+//     iteration ends with s_waitcnt vmcnt(2 * kLoadsPerIter) (loads complete
+//     in issue order; every iteration issues the same loads, tiles past the
+//     item reading zero) and a fence-free barrier. Page ids are read two
+//     iterations ahead. With page_size a power of two >= 16 a wave's rows of a
+//     tile lie in one page: one descriptor per wave and tile, ranged to the
+//     valid tokens so that tokens past the item read as zero; other page
+//     sizes look up every token and repeat the last valid one past the end
+//     (its weight is exactly 0).
 //   * LDS rows are 256 B (one token's 128 values, unpadded) with the 16-byte
 //     chunks XOR-swizzled per row: K by (row mod 16), V by 4 * (row mod 4).
 //     Neither the K operand reads (32 rows, one chunk) nor the transposing V
@@ -39,8 +43,14 @@
 //     is taken straight from the score registers (the token order inside a
 //     16-token step is permuted identically on both operands); the fp32
 //     accumulator of row l % 32 stays in lane l, so the rescale is lane-local.
+//   * Software pipeline: iteration j computes S(j+1) on the MFMAs while the
+//     VALU forms tile j's weights, then tile j's PV product runs beside the
+//     row maxima of tile j+1; the reference exponent of a row moves only when
+//     a score exceeds it by more than 2^8 (lazy rescaling).
 //   * The scale multiplies the fp32 scores (q is not pre-scaled), in the
-//     log2 domain; LSE = (m + log2 l) * ln 2.
+//     log2 domain, fused with the subtraction of the reference; LSE =
+//     (m + log2 l) * ln 2. A split item writes its partial state as O and the
+//     pair (m, l).
 //   * Variants (VAR instances; the FlashInfer article, section "Custom
 //     attention templates", names them): a tile's scores are soft-capped as
 //     soon as they leave the MFMAs, before the mask; the sliding window masks
