@@ -138,8 +138,15 @@ def test_prefill_generic_pages_unmasked(pkv, ws):
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("sched", [None, (256, 16, 16)])
 def test_cascade(pkv, ws, sched):
+    """With (256, 16, 16) the rows average 32+ states (prefix chunks and suffix chunks), so the
+    merge runs its four-waves-per-row mapping with the prefix states."""
     sfx = [64, 1, 900, 0, 3000]
     pre = 2000
+    if sched is not None:
+        from oracle.plan import cascade_spec
+        _l0, l1, base = cascade_spec(pre, sfx, 16, 8, 4, sched, sched)
+        states = sum(g[4] for g in l1.merge_groups) + sum(bs[1] for bs in base)
+        assert states >= 32 * len(l1.merge_groups)
     w = wl.cascade(seed=840, batch=len(sfx), prefix_len=pre, suffix_lens=sfx)
     w.q = extreme_q(w.q, w.dtype)
     extreme_paged(w.kv, w.dtype, sfx, extra=(w.prefix_indices, pre))
