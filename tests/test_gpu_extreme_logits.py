@@ -20,6 +20,10 @@ and the test measures the softmax path, not the dot product.
 
 LSE is ~5.2e4 here, where fp32 itself carries ~4e-3 absolute, so LSE is held to
 1e-6 relative (0.05 absolute); O is held to the dtype tolerance.
+
+The variant cases add a sliding window and per-head sinks a few units around the
+logits (so a sink's weight is comparable to the keys'), split and unsplit, against
+the variant oracle.
 """
 
 import math
@@ -214,3 +218,66 @@ def test_pod(pkv, ws):
         O, LSE = run_oracle(part)
         check_extreme(part, o.float().cpu().numpy().astype(np.float64),
                       lse.cpu().numpy().astype(np.float64), O, LSE, f"extreme mixed batch, {name}")
+
+
+# ----------------------------------------------------------------------------
+# variants at the same magnitudes: a sliding window, and sinks near the logits
+# (the sink's weight is comparable to the keys', so it moves every row)
+# ----------------------------------------------------------------------------
+def _extreme_sinks(seed, Hq):
+    """float32 sinks a few units around the extreme inputs' logits (natural log)."""
+    rng = np.random.default_rng(seed)
+    return (-52140.0 + 3.0 * rng.standard_normal(Hq)).astype(np.float32)
+
+
+@pytest.mark.parametrize("sched", [None, (1024, 8, 16)])
+def test_decode_window_and_sinks(pkv, ws, sched):
+    from oracle import variants as ov
+    lens = [1, 40, 700, 2500]
+    w = wl.batch_decode(seed=870, kv_lens=lens, num_qo_heads=16, num_kv_heads=4, page_size=16,
+                        dtype="f16")
+    w.q = extreme_q(w.q, w.dtype)
+    extreme_paged(w.kv, w.dtype, lens)
+    wl.canary_tails(w.kv, w.dtype)
+    W, sinks = 300, _extreme_sinks(871, 16)
+    say(f"[case] extreme decode W={W} sinks sched={sched}")
+    up = Uploaded(w)
+    plan = pkv.pkv_decode_plan(w.kv.kv_indptr, w.kv.last_page_len, 16, 4, 128, 16, up.q.dtype, ws,
+                               sched=sched, window_left=W)
+    o, lse = pkv.pkv_decode_run(plan, up.q, up.k, up.v, up.kv_indptr, up.kv_indices, w.sm_scale,
+                                window_left=W, sinks=torch.from_numpy(sinks).cuda())
+    torch.cuda.synchronize()
+    kv = w.kv
+    O, LSE = ov.batch_decode_variant(w.q, kv.k_cache, kv.v_cache, kv.kv_indptr, kv.kv_indices,
+                                     kv.last_page_len, w.dtype, w.sm_scale, window_left=W,
+                                     sinks=sinks)
+    check_extreme(w, o.float().cpu().numpy().astype(np.float64),
+                  lse.cpu().numpy().astype(np.float64), O, LSE,
+                  f"extreme decode, window and sinks, sched={sched}")
+
+
+@pytest.mark.parametrize("sched", [None, (64, 1, 16)])
+def test_prefill_window_and_sinks(pkv, ws, sched):
+    from oracle import variants as ov
+    qo, kv_lens = [40, 130, 1], [700, 300, 1]
+    w = prefill_with_lengths(seed=872, qo_lens=qo, kv_lens=kv_lens, Hq=16, Hkv=4, P=16,
+                             dtype="bf16")
+    w.q = extreme_q(w.q, w.dtype)
+    extreme_paged(w.kv, w.dtype, kv_lens)
+    wl.canary_tails(w.kv, w.dtype)
+    W, sinks = 100, _extreme_sinks(873, 16)
+    say(f"[case] extreme prefill W={W} sinks sched={sched}")
+    up = Uploaded(w)
+    plan = pkv.pkv_prefill_plan(w.qo_indptr, w.kv.kv_indptr, w.kv.last_page_len, 16, 4, 128, 16,
+                                up.q.dtype, True, ws, sched=sched, window_left=W)
+    o, lse = pkv.pkv_prefill_run(plan, up.q, up.k, up.v, up.qo_indptr, up.kv_indptr,
+                                 up.kv_indices, w.sm_scale, window_left=W,
+                                 sinks=torch.from_numpy(sinks).cuda())
+    torch.cuda.synchronize()
+    kv = w.kv
+    O, LSE = ov.batch_prefill_variant(w.q, kv.k_cache, kv.v_cache, w.qo_indptr, kv.kv_indptr,
+                                      kv.kv_indices, kv.last_page_len, w.dtype, w.sm_scale, True,
+                                      window_left=W, sinks=sinks)
+    check_extreme(w, o.float().cpu().numpy().astype(np.float64),
+                  lse.cpu().numpy().astype(np.float64), O, LSE,
+                  f"extreme prefill, window and sinks, sched={sched}")
