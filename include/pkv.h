@@ -392,7 +392,8 @@ pkv_status pkv_prefill_run_timed(const pkv_plan_info* plan, const void* q, const
  * a split KV head is merged by a second launch. float_ws holds the partial
  * states: float_ws_required bytes (pass NULL, 0 to query; 0 when nothing
  * splits); calls that share a workspace must not overlap. The contiguous
- * cache is handled as 16-token pages.
+ * cache is handled as 16-token pages. With kv_len 0, k and v may be NULL
+ * (nothing is read) and every row is O = 0, LSE = -inf.
  * ------------------------------------------------------------------------- */
 pkv_status pkv_single_decode(const void* q, const void* k, const void* v, int32_t kv_len,
                              int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,

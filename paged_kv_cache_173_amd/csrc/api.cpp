@@ -887,8 +887,8 @@ pkv_status pkv_single_decode(const void* q, const void* k, const void* v, int32_
   if (need > 0 && (float_ws == nullptr || float_ws_bytes < static_cast<size_t>(need)))
     return fail(PKV_ERR_WORKSPACE_TOO_SMALL, "float workspace too small: need " +
                                                  std::to_string(need) + " B");
-  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr)
-    return fail(PKV_ERR_INVALID_ARG, "q, k, v or o is NULL");
+  if (q == nullptr || o == nullptr || (kv_len > 0 && (k == nullptr || v == nullptr)))
+    return fail(PKV_ERR_INVALID_ARG, "q, o, or (kv_len > 0) k or v is NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(float_ws))
     return fail(PKV_ERR_INVALID_ARG, "q, k, v, o and float_ws must be 16-byte aligned");
   hipStream_t hs = static_cast<hipStream_t>(stream);

@@ -191,6 +191,12 @@ def test_single_decode_reports_workspace_and_validates(lib):
     st = lib._lib_single_decode(None, None, None, -1, 32, 32, 128, 0, 0.1, ctypes.byref(s), None,
                                 0, ctypes.byref(need), None, None, None)
     assert st == lib.PKV_ERR_INVALID_ARG
+    # a non-empty cache needs k and v (checked before any launch; q and o are stand-ins)
+    fake = ctypes.c_void_p(0x10000)
+    st = lib._lib_single_decode(fake, None, None, 5, 32, 32, 128, 0, 0.1, ctypes.byref(s), None,
+                                0, ctypes.byref(need), fake, None, None)
+    assert st == lib.PKV_ERR_INVALID_ARG
+    assert "k or v is NULL" in lib.pkv_last_error()
 
 
 def test_cascade_plan_validation(lib):
