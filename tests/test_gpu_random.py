@@ -1,4 +1,4 @@
-"""GPU parity on seeded random configurations of every planned entry point.
+"""GPU parity on seeded random configurations of every entry point.
 
 Each case draws its shape from its own seed: dtype, KV heads, GQA group, page size
 (page-uniform and generic kernels), batch, a length mix with empty requests, causal
@@ -6,7 +6,10 @@ or not, and a schedule (the device default or a random one that splits more or l
 Pools carry NaN canaries in unused pages and past every request's last token, so any
 read of a wrong page or slot poisons the output. Every output row is compared with the
 fp64 oracle at the dtype's tolerance. The cases are ordinary coverage of the shape
-space, sized so the oracle finishes each in well under a second.
+space, sized so the oracle finishes each in well under a second. Block-sparse, append,
+the variants and the mixed launch reuse the checks of their own test modules (append:
+every byte of both pools; mixed launch: bit-identical to separate runs and within
+tolerance of the oracle); merge_states is checked against the oracle's merge.
 """
 
 import math
@@ -114,3 +117,100 @@ def test_random_single_decode(pkv, ws, case):
     w = wl.single_decode(seed=9800 + case, kv_len=L, num_qo_heads=G * Hkv, num_kv_heads=Hkv,
                          dtype=dtype)
     _check(pkv, ws, w, _sched(rng), f"random single decode {case} L={L}")
+
+
+# ----------------------------------------------------------------------------
+# the other entry points, with the helpers of their own test modules
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("case", range(8))
+def test_random_block_sparse(pkv, ws, case):
+    from test_gpu_block_sparse import check
+    rng = np.random.default_rng(9900 + case)
+    R, C = int(rng.choice([1, 7, 16, 64, 100, 128])), int(rng.choice([5, 16, 32, 64, 128]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    nq, nkv = int(rng.integers(1, 400)), int(rng.integers(1, 700))
+    mb = (nq + R - 1) // R
+    empty = tuple(int(i) for i in rng.choice(mb, size=min(mb, 2), replace=False)) \
+        if rng.random() < 0.5 else ()
+    w = wl.block_sparse(seed=10000 + case, num_qo_tokens=nq, num_kv_tokens=nkv, row_block=R,
+                        col_block=C, density=float(rng.uniform(0.05, 0.9)),
+                        num_qo_heads=G * Hkv, num_kv_heads=Hkv,
+                        dtype=str(rng.choice(["f16", "bf16"])), diagonal=bool(rng.random() < 0.5),
+                        empty_rows=empty)
+    check(pkv, ws, w, f"random block-sparse {case}")
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_append(pkv, case):
+    from test_gpu_append import run_case
+    rng = np.random.default_rng(10100 + case)
+    n = int(rng.integers(1, 9))
+    w = wl.append_kv(seed=10200 + case, new_lens=rng.integers(0, 90, size=n),
+                     prefix_lens=rng.integers(0, 200, size=n),
+                     num_kv_heads=int(rng.choice([1, 2, 3, 8, 32])),
+                     page_size=int(rng.choice(PAGE_SIZES)), dtype=str(rng.choice(["f16", "bf16"])),
+                     canary=True)
+    run_case(pkv, w, f"random append {case}")
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_variants(pkv, ws, case):
+    from test_gpu_variants import run_decode, run_prefill
+    rng = np.random.default_rng(10300 + case)
+    dtype = str(rng.choice(["f16", "bf16"]))
+    Hkv, G = int(rng.choice([1, 2, 4])), int(rng.choice([1, 2, 4, 8]))
+    P = int(rng.choice(PAGE_SIZES))
+    W = int(rng.choice([-1, 0, 5, 64, 300]))
+    cap = float(rng.choice([0.0, 2.0, 30.0]))
+    sinks = ((rng.standard_normal(G * Hkv) * 2.0).astype(np.float32)
+             if rng.random() < 0.6 else None)
+    sched = _sched(rng)
+    lens = _lengths(rng, int(rng.integers(1, 8)), 900)
+    wd = wl.batch_decode(seed=10400 + case, kv_lens=lens, num_qo_heads=G * Hkv, num_kv_heads=Hkv,
+                         page_size=P, dtype=dtype, canary=True)
+    run_decode(pkv, ws, wd, W=W, cap=cap, sinks=sinks, sched=sched,
+               label=f"random decode variant {case}")
+    n = int(rng.integers(1, 5))
+    qo = rng.integers(1, 200, size=n)
+    wp = prefill_with_lengths(seed=10500 + case, qo_lens=qo, kv_lens=qo + rng.integers(0, 500, n),
+                              Hq=G * Hkv, Hkv=Hkv, P=P, dtype=dtype,
+                              causal=bool(rng.random() < 0.75))
+    run_prefill(pkv, ws, wp, W=W, cap=cap, sinks=sinks, sched=sched,
+                label=f"random prefill variant {case}")
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_random_mixed_batch(pkv, ws, case):
+    from test_gpu_pod import run_case
+    rng = np.random.default_rng(10600 + case)
+    Hkv, G = int(rng.choice([1, 2, 4, 8])), int(rng.choice([1, 2, 4, 8, 16]))
+    npf, nd = int(rng.integers(0, 4)), int(rng.integers(0, 9))
+    w = wl.pod(seed=10700 + case, qo_lens=rng.integers(1, 200, size=npf),
+               prefix_lens=rng.integers(0, 400, size=npf), d_lens=_lengths(rng, nd, 1500),
+               num_qo_heads=G * Hkv, num_kv_heads=Hkv, page_size=int(rng.choice(PAGE_SIZES)),
+               dtype=str(rng.choice(["f16", "bf16"])), causal=bool(rng.random() < 0.75),
+               canary=True)
+    run_case(pkv, ws, w, f"random mixed batch {case}", sched=_sched(rng))
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_random_merge_states(pkv, case):
+    import oracle
+    rng = np.random.default_rng(10800 + case)
+    g = torch.Generator().manual_seed(10900 + case)
+    dtype = [torch.float16, torch.bfloat16, torch.float32][case % 3]
+    n, K, H = int(rng.integers(1, 70)), int(rng.integers(1, 20)), int(rng.choice([1, 3, 8]))
+    say(f"[case] random merge_states {case}: n={n} K={K} H={H} {dtype}")
+    v = torch.randn(n, K, H, 128, generator=g).to(dtype)
+    s = torch.randn(n, K, H, generator=g) * float(rng.choice([1.0, 10.0, 1000.0]))
+    s[torch.rand(n, K, H, generator=g) < 0.2] = -float("inf")
+    vo, so = pkv.pkv_merge_states(v.cuda(), s.cuda())
+    torch.cuda.synchronize()
+    O, LSE = oracle.merge_states(v.double().numpy(), s.double().numpy())
+    tol = {torch.float16: 2e-3, torch.bfloat16: 1e-2, torch.float32: 1e-5}[dtype]
+    assert np.abs(vo.double().cpu().numpy() - O).max() <= tol
+    fin = np.isfinite(LSE)
+    so = so.cpu().numpy()
+    assert np.array_equal(np.isneginf(so), ~fin)
+    assert np.abs(so[fin] - LSE[fin]).max() <= 1e-5 * max(1.0, float(np.abs(LSE[fin]).max()))
