@@ -215,7 +215,8 @@ pkv_status pkv_default_sched(int32_t device, pkv_sched* out);
  * prefill: occ (one wave of items covers the chip); decode: (5*occ+1)/2, about
  * two and a half waves of items, so that the longest-first order evens out the
  * last one. A plan given a NULL sched uses this for its own kind (the
- * cascade: prefill for level 0, decode for level 1). Needs a GPU. */
+ * cascade: decode for level 1, and for level 0 the prefill schedule with
+ * wg_per_cu = 1, one item per CU). Needs a GPU. */
 pkv_status pkv_default_sched_for(pkv_kind kind, int32_t device, pkv_sched* out);
 
 /* ---------------------------------------------------------------------------
@@ -453,8 +454,10 @@ pkv_status pkv_merge_states(const void* v, const float* s, int32_t n, int32_t nu
  * prefix states (base_slot_begin, base_num_chunks, base_row of its group
  * record: the level-0 slots and first row that hold its rows) with its suffix
  * chunks into o [batch, Hq, 128] (cache dtype) and lse [batch, Hq] or NULL.
- * Three launches in all. Runs of one plan must not overlap (see
- * pkv_decode_run).
+ * A non-NULL sched applies to both levels; with NULL, level 1 takes the
+ * decode default and level 0 the prefill default with wg_per_cu = 1 (see
+ * pkv_default_sched_for). Three launches in all. Runs of one plan must not
+ * overlap (see pkv_decode_run).
  * ------------------------------------------------------------------------- */
 pkv_status pkv_cascade_plan(int32_t prefix_num_pages, int32_t prefix_last_page_len,
                             const int32_t* suffix_indptr_h, const int32_t* suffix_last_page_len_h,

@@ -50,6 +50,9 @@ level-0 states of its G rows: packed rows b*G .. b*G + G - 1 of KV head g at
 level 0, i.e. tile t = (b*G) // 128 from row (b*G) % 128 on (rows past 127 are
 the next tile's first rows), whose n0 chunk slots start at (t * Hkv + g) * n0
 (n0: the chunks of every level-0 group, which all have the same extent).
+``cascade_spec`` takes the two levels' schedules explicitly; with no schedule
+the library uses the decode default for level 1 and the prefill default with
+wg_per_cu = 1 (one level-0 item per CU) for level 0.
 """
 
 from __future__ import annotations

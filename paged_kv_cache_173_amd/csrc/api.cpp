@@ -1071,6 +1071,10 @@ pkv_status pkv_cascade_plan(int32_t prefix_num_pages, int32_t prefix_last_page_l
   pkv_sched s0, s1;
   if ((st = resolve_sched(sched, PKV_KIND_PREFILL, &s0))) return st;
   if ((st = resolve_sched(sched, PKV_KIND_DECODE, &s1))) return st;
+  // Default level 0: one item per CU. Its items all run in one round whatever
+  // their number, so half as many prefix chunks as the prefill default halve
+  // the states it writes and the merge reads.
+  if (sched == nullptr) s0.wg_per_cu = 1;
   std::vector<int64_t> pre_qo(1, batch), suf_qo(batch, 1);
   pkv::HostPlan hp0, hp1;
   std::string err;

@@ -186,6 +186,31 @@ def test_device_plan_tables_equal_the_spec(pkv, ws):
     assert [tuple(r[:5]) for r in groups.tolist()] == spec.merge_groups
 
 
+def test_default_cascade_plan_levels(pkv, ws):
+    """With no schedule the cascade plans level 1 by the decode default and level 0 by the
+    prefill default with one item per CU (wg_per_cu = 1); both levels' device tables equal
+    the oracle's cascade rule for those schedules."""
+    from oracle.plan import cascade_spec
+    w = wl.FULL[3]()
+    kv, B = w.kv, len(w.kv.kv_lens)
+    pre_pages = len(w.prefix_indices)
+    plan = pkv.pkv_cascade_plan(pre_pages, w.prefix_last_page_len, kv.kv_indptr,
+                                kv.last_page_len, 32, 8, 128, 16, torch.float16, ws)
+    sp = pkv.pkv_default_sched_for(pkv.PKV_KIND_PREFILL)
+    sd = pkv.pkv_default_sched_for(pkv.PKV_KIND_DECODE)
+    s0 = (sp.num_cus, 1, sp.min_chunk_tokens)
+    s1 = (sd.num_cus, sd.wg_per_cu, sd.min_chunk_tokens)
+    pre_len = (pre_pages - 1) * 16 + w.prefix_last_page_len
+    level0, level1, base = cascade_spec(pre_len, kv.kv_lens, 16, 8, 4, s0, s1)
+    assert plan.part[0].num_items == len(level0.items) == sp.num_cus
+    for part, spec in ((0, level0), (1, level1)):
+        items, groups = pkv.read_plan_tables(plan, ws, part)
+        assert [tuple(r) for r in items.tolist()] == spec.items, part
+        assert [tuple(r[:5]) for r in groups.tolist()] == spec.merge_groups, part
+        if part == 1:
+            assert [tuple(r[5:]) for r in groups.tolist()] == base
+
+
 def test_runs_are_bitwise_reproducible(pkv, ws):
     w = wl.SMALL[1]()
     up = Uploaded(w)
