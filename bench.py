@@ -53,12 +53,14 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# Sources the decode kernel is compiled from; a traffic figure in profiles/ is
-# used only while their hash matches the one recorded next to it.
+# Sources the decode kernel and its plan come from; a traffic figure in profiles/
+# is used only while their hash matches the one recorded next to it.
 DECODE_SOURCES = ["paged_kv_cache_173_amd/csrc/decode.hip",
                   "paged_kv_cache_173_amd/csrc/decode_item.h",
                   "paged_kv_cache_173_amd/csrc/device_common.h",
-                  "paged_kv_cache_173_amd/csrc/kernels.h"]
+                  "paged_kv_cache_173_amd/csrc/kernels.h",
+                  "paged_kv_cache_173_amd/csrc/planner.cpp",
+                  "paged_kv_cache_173_amd/csrc/api.cpp"]
 TRAFFIC_PROFILE = "profiles/decode_kernel_batch64_fp16_hbm_traffic.md"
 
 

@@ -212,7 +212,7 @@ pkv_status pkv_default_sched(int32_t device, pkv_sched* out);
 
 /* Defaults tuned to one kernel: as pkv_default_sched, but wg_per_cu follows
  * the number of workgroups of that kind's kernel resident on one CU (occ):
- * prefill: occ (one wave of items covers the chip); decode: (5*occ+1)/2, about
+ * prefill: occ (one wave of items covers the chip); decode: (5*occ)/2, about
  * two and a half waves of items, so that the longest-first order evens out the
  * last one. A plan given a NULL sched uses this for its own kind (the
  * cascade: decode for level 1, and for level 0 the prefill schedule with

@@ -565,11 +565,11 @@ pkv_status pkv_default_sched_for(pkv_kind kind, int32_t device, pkv_sched* out) 
   if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return hip_fail(e, "hipSetDevice");
   const int32_t occ = kind == PKV_KIND_DECODE ? pkv::decode_occupancy() : pkv::prefill_occupancy();
   if (cur != device) (void)hipSetDevice(cur);
-  // Decode: about two and a half waves of items per resident workgroup, so that
-  // the longest-first order evens out the last wave (one wave left ~5 % idle at
-  // the end on the 64-request and 4 x 128k-token workloads). Prefill: one wave;
-  // its tiles already give several items per workgroup.
-  if (occ > 0) out->wg_per_cu = kind == PKV_KIND_DECODE ? (5 * occ + 1) / 2 : occ;
+  // Decode: about two and a half waves of items per resident workgroup (rounded
+  // down), so that the longest-first order evens out the last wave (one wave
+  // left ~5 % idle at the end on the 64-request and 4 x 128k-token workloads).
+  // Prefill: one wave; its tiles already give several items per workgroup.
+  if (occ > 0) out->wg_per_cu = kind == PKV_KIND_DECODE ? (5 * occ) / 2 : occ;
   return ok();
 }
 
