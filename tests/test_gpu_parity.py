@@ -192,7 +192,7 @@ def test_default_cascade_plan_levels(pkv, ws):
     the oracle's cascade rule for those schedules."""
     from oracle.plan import cascade_spec
     w = wl.FULL[3]()
-    kv, B = w.kv, len(w.kv.kv_lens)
+    kv = w.kv
     pre_pages = len(w.prefix_indices)
     plan = pkv.pkv_cascade_plan(pre_pages, w.prefix_last_page_len, kv.kv_indptr,
                                 kv.last_page_len, 32, 8, 128, 16, torch.float16, ws)
