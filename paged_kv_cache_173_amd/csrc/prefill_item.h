@@ -157,7 +157,7 @@ __shared__ __attribute__((aligned(1024))) char sV3[kTileBytes];
 // rows 32*RB*w .. 32*RB*(w+1)-1 of an item of 32*NW*RB rows, in RB blocks of
 // 32. The NW waves share every K / V tile (each stages KT/NW of its rows). Every K and V operand read from LDS
 // feeds RB MFMAs (one per block). The kernels use RB = 1 (two waves per SIMD,
-// 256 VGPRs). RB = 2 halves the LDS reads per MFMA but needs about 330
+// 187-221 VGPRs by instance). RB = 2 halves the LDS reads per MFMA but needs about 330
 // registers per lane, so one wave per SIMD; with the compiler placing the
 // score accumulators in AGPRs (every softmax touch then copies them out) it
 // gave bit-identical results 23 % slower on the causal prefill workload.
@@ -474,46 +474,6 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
       for (int mb = 0; mb < 4; ++mb) acc[rb][mb] *= alpha;
     }
   };
-  // Weights of a tile, rounded to the storage dtype: pk[rb][st] is the B
-  // operand of 16-token step st of block rb's PV product.
-  auto weights = [&](const f32x16 (&s)[RB], u32x4 (&pk)[RB][2]) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float sum = l_run[rb], xsum = l_lse[rb];
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float x0 = fast_exp2(fmaf(s[rb][8 * st + 2 * j], a.scale_log2, neg_m[rb]));
-          const float x1 = fast_exp2(fmaf(s[rb][8 * st + 2 * j + 1], a.scale_log2, neg_m[rb]));
-          pk[rb][st][j] = T::pack2(x0, x1);
-          sum = T::add_pair(pk[rb][st][j], sum);
-          if constexpr (kExactLse) xsum += x0 + x1;
-        }
-      }
-      l_run[rb] = sum;
-      l_lse[rb] = xsum;
-    }
-  };
-  // O^T += V^T P^T over two 16-token steps. Step st covers tokens
-  // 16st + 4*half + {0..3} (first read) and + {8..11} (second read), the
-  // order in which pk[rb][st] holds them.
-  auto pv = [&](const char* vt, const u32x4 (&pk)[RB][2]) {
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const char* p = vt + 4096 * st + va[mb];
-        const s16x4 lo = lds_read_tr16_b64(p);
-        const s16x4 hi = lds_read_tr16_b64(p + 8 * kRowBytes);
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        const u32x4 vfr = u32x4{l2[0], l2[1], h2[0], h2[1]};
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) acc[rb][mb] = T::mfma_32x32x16(vfr, pk[rb][st], acc[rb][mb]);
-      }
-    }
-  };
-
   // The two halves of a pipelined iteration. The instruction order is written
   // out: each step issues an LDS read two MFMA steps ahead of its use, one MFMA
   // per block, and a slice of the VALU work of the other tile, and a
@@ -586,7 +546,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
   // PV of tile j (8 MFMA steps) with the lane maxima of tile j+1's scores, one
   // pair per block and step; leaves the lane maxima (raw scores) in t.
   auto pv_max = [&](const char* vt, u32x4 (&vf)[3], const u32x4 (&pk)[RB][2],
-                    const f32x16 (&sn)[RB], float (&t)[RB]) {
+                    const f32x16 (&sn)[RB], float (&t)[RB], auto&& hook) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) t[rb] = neg_inf();
 #pragma unroll
@@ -600,6 +560,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
         t[rb] = fmaxf(fmaxf(t[rb], sn[rb][2 * i]), sn[rb][2 * i + 1]);
         asm volatile("" : "+v"(t[rb]));   // likewise for the running maxima
       }
+      if (i == 4) hook();
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -619,24 +580,24 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
   // Page ids of the K loads of tiles j+4 and j+5 and of the V load of tile j+3.
   Pids pid_k0, pid_k1, pid_v;
   Group grp_v{0, 0};   // uniform mode: where the V load of tile j+3 reads
+  Group grp_k{0, 0};   // uniform mode: where the K load of tile j+4 reads
   // `ph` is j % 4 as a compile-time constant, so buffer choices are constants.
-  auto body = [&](int j, auto ph, f32x16 (&s_cur)[RB], f32x16 (&s_nxt)[RB], bool has_next) {
+  auto body = [&](int j, auto ph, f32x16 (&s_cur)[RB], f32x16 (&s_nxt)[RB]) {
     constexpr int p = decltype(ph)::value;
     char* kn = kbuf(std::integral_constant<int, p>{});                  // receives K(j+4)
     char* vn = vbuf(std::integral_constant<int, (p + 3) & 3>{});        // receives V(j+3)
     const char* kt = kbuf(std::integral_constant<int, (p + 1) & 3>{});  // holds K(j+1)
     const char* vt = vbuf(std::integral_constant<int, p>{});            // holds V(j)
     u32x4 kf[3], vf[3];
-    if (has_next) {   // the first K operands land while the loads below are issued
-      kf[0] = k_read(kt, 0);
-      kf[1] = k_read(kt, 1);
-    }
+    // The first K operands land while the loads below are issued.
+    kf[0] = k_read(kt, 0);
+    kf[1] = k_read(kt, 1);
+    __builtin_amdgcn_sched_barrier(0);
     const Pids pnn = fetch_pids(j + 6);
     if constexpr (MODE == kPagedUniform) {
-      const Group gk = group_of(j + 4, pid_k0);
-      issue_group(gk, kbase, kn, true);
+      issue_group(grp_k, kbase, kn, true);
       issue_group(grp_v, vbase, vn, false);
-      grp_v = gk;
+      grp_v = grp_k;
     } else {
       issue(j + 4, pid_k0, kbase, kn, true);
       issue(j + 3, pid_v, vbase, vn, false);
@@ -646,20 +607,19 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
     pid_k1 = pnn;
 
     u32x4 pk[RB][2];
-    if (has_next) {
-      qk_weights(kt, kf, s_nxt, s_cur, pk, vt, vf);
-      // The weights are complete here (kept from sinking past the branch).
+    qk_weights(kt, kf, s_nxt, s_cur, pk, vt, vf);
+    // The weights are complete here (kept from sinking past the branch).
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) asm volatile("" ::"v"(pk[rb][0]), "v"(pk[rb][1]));
-      mask(j + 1, s_nxt);
-      float t[RB];
-      pv_max(vt, vf, pk, s_nxt, t);
+    for (int rb = 0; rb < RB; ++rb) asm volatile("" ::"v"(pk[rb][0]), "v"(pk[rb][1]));
+    mask(j + 1, s_nxt);
+    float t[RB];
+    // The next iteration's K group is formed among the PV MFMAs, so that its
+    // scalar address arithmetic is off the path to the next tile's loads.
+    pv_max(vt, vf, pk, s_nxt, t, [&] {
+      if constexpr (MODE == kPagedUniform) grp_k = group_of(j + 5, pid_k0);
+    });
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) maybe_rescale(rb, t[rb]);
-    } else {
-      weights(s_cur, pk);
-      pv(vt, pk);
-    }
+    for (int rb = 0; rb < RB; ++rb) maybe_rescale(rb, t[rb]);
     wait_vm<2 * kLoadsPerIter>();
     lds_barrier();
   };
@@ -682,7 +642,10 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
     issue(3, p3, kbase, sK3, true);
     issue(2, p2, vbase, sV2, false);
     pid_v = p3;
-    if constexpr (MODE == kPagedUniform) grp_v = group_of(3, p3);
+    if constexpr (MODE == kPagedUniform) {
+      grp_v = group_of(3, p3);
+      grp_k = group_of(4, pid_k0);
+    }
     // K(0), V(0) and K(1) have landed (2 * kLoadsPerIter loads follow K(1));
     // p4, K(2), V(1), p5, K(3), V(2) may still be in flight.
     wait_vm<2 * kLoadsPerIter>();
@@ -699,21 +662,19 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
     constexpr std::integral_constant<int, 1> ph1{};
     constexpr std::integral_constant<int, 2> ph2{};
     constexpr std::integral_constant<int, 3> ph3{};
-    int j = 0;
-    for (; j + 4 < ntiles; j += 4) {   // four tiles, each with a successor
-      body(j, ph0, sA, sB, true);
-      body(j + 1, ph1, sB, sA, true);
-      body(j + 2, ph2, sA, sB, true);
-      body(j + 3, ph3, sB, sA, true);
-    }
-    // The last one to four tiles.
-    body(j, ph0, sA, sB, j + 1 < ntiles);
-    if (j + 1 < ntiles) {
-      body(j + 1, ph1, sB, sA, j + 2 < ntiles);
-      if (j + 2 < ntiles) {
-        body(j + 2, ph2, sA, sB, j + 3 < ntiles);
-        if (j + 3 < ntiles) body(j + 3, ph3, sB, sA, false);
-      }
+    // Every tile runs the same body, the last one included: its "next" tile
+    // lies past the item (its K buffer holds zeros or repeated rows, already
+    // waited for like any other), every score of it is masked to -inf, so it
+    // moves no reference and its scores are dropped when the loop ends.
+    for (int j = 0;; j += 4) {
+      body(j, ph0, sA, sB);
+      if (j + 1 == ntiles) break;
+      body(j + 1, ph1, sB, sA);
+      if (j + 2 == ntiles) break;
+      body(j + 2, ph2, sA, sB);
+      if (j + 3 == ntiles) break;
+      body(j + 3, ph3, sB, sA);
+      if (j + 4 == ntiles) break;
     }
   }
 
