@@ -95,6 +95,21 @@ def test_prefill_page_sizes_and_head_ratios(pkv, ws, P, heads):
                sched=(256, 4, 64))
 
 
+@pytest.mark.parametrize("P", [5, 16])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_prefill_item_tile_counts(pkv, ws, P, dtype):
+    """Items of 1 to 9 KV tiles (32 tokens each), so that an item ends at every one of
+    the four positions of the kernel's four-tile unrolled loop, with and without a KV
+    split. The tile after an item's last one is scored and fully masked; it must not
+    change any row."""
+    kv_lens = [1, 31, 32, 33, 64, 95, 96, 97, 128, 129, 160, 191, 255, 256, 257, 288]
+    qo_lens = [min(8, n) for n in kv_lens]
+    w = prefill_with_lengths(seed=17 + P, qo_lens=qo_lens, kv_lens=kv_lens, Hq=8, Hkv=2, P=P,
+                             dtype=dtype)
+    _check(pkv, ws, w, f"prefill tile counts P={P} {dtype}")
+    _check(pkv, ws, w, f"prefill tile counts P={P} {dtype} split", sched=(256, 8, 16))
+
+
 def test_prefill_query_longer_than_kv_masks_leading_rows(pkv, ws):
     """Q > L: the first Q - L query rows see no key and must be (0, -inf)."""
     w = prefill_with_lengths(seed=5, qo_lens=[40, 3], kv_lens=[10, 0], Hq=8, Hkv=2, P=16)
