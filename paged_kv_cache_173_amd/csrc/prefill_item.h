@@ -120,17 +120,16 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Stores 4 consecutive output values (rounded once to OUT).
+// Stores 4 consecutive output values (rounded once to OUT, nearest even; a
+// 16-bit OUT is packed two values per conversion).
 template <class OUT>
 __device__ __forceinline__ void store4(OUT* p, float x0, float x1, float x2, float x3) {
   if constexpr (sizeof(OUT) == 4) {
     *reinterpret_cast<f32x4*>(p) = f32x4{x0, x1, x2, x3};
   } else {
-    const uint32_t a = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, out_cast<OUT>(x0))) |
-                       (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, out_cast<OUT>(x1))) << 16);
-    const uint32_t b = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, out_cast<OUT>(x2))) |
-                       (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, out_cast<OUT>(x3))) << 16);
-    *reinterpret_cast<u32x2*>(p) = u32x2{a, b};
+    using S = std::conditional_t<std::is_same_v<OUT, __bf16>, BF16, F16>;
+    static_assert(std::is_same_v<OUT, typename S::elem>, "16-bit outputs are fp16 or bf16");
+    *reinterpret_cast<u32x2*>(p) = u32x2{S::pack2(x0, x1), S::pack2(x2, x3)};
   }
 }
 
@@ -701,7 +700,7 @@ __device__ __forceinline__ void prefill_item(const PrefillArgs& a, const int32_t
         }
       }
     }
-    const float inv = l_tot > 0.f ? o_scale / l_tot : 0.f;
+    const float inv = l_tot > 0.f ? o_scale * __builtin_amdgcn_rcpf(l_tot) : 0.f;
     if (slot < 0) {
       const float lse = l_ex > 0.f ? (m_fin + fast_log2(l_ex)) * kLn2 : neg_inf();
       const int64_t orow = static_cast<int64_t>(q0 + qtok[rb]) * a.num_qo_heads + head[rb];
