@@ -36,7 +36,8 @@ import oracle
 from paged_kv_cache_173_amd import workloads as wl
 
 from extreme_inputs import LOGIT_CEILING, _bits, _float, _quarter, _ramp, extreme_paged, extreme_q, extreme_rows
-from gpu_common import TOL, Uploaded, dev, dev_i32, prefill_with_lengths, run_gpu, run_oracle, say
+from gpu_common import (TOL, Uploaded, dev, dev_i32, output_error, prefill_with_lengths, run_gpu,
+                        run_oracle, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -59,12 +60,12 @@ def check_extreme(w, o, lse, O, LSE, label):
     assert (LSE[fin] < LOGIT_CEILING).all(), "the inputs must put every logit below -5e4"
     assert np.array_equal(np.isneginf(lse), np.isneginf(LSE)), f"{label}: -inf rows differ"
     assert not np.isnan(o).any(), f"{label}: NaN in output"
-    err_o = float(np.max(np.abs(o - O)))
+    err_o, excess, at = output_error(o, O, w.dtype, to)
     rel_l = float(np.max(np.abs(lse[fin] - LSE[fin]) / np.abs(LSE[fin])))
     say(f"  {label}: max|dO| = {err_o:.3e} (tol {to}), max rel dLSE = {rel_l:.2e} (tol 1e-6), "
         f"max|O| = {float(np.max(np.abs(O))):.3f}")
     assert rel_l <= 1e-6, f"{label}: LSE relative error {rel_l}"
-    assert err_o <= to, f"{label}: output error {err_o} > {to}"
+    assert excess <= 0, f"{label}: output error {err_o}: {excess:.3e} over the bound at |O| = {at:.4f}"
     assert float(np.max(np.abs(O[fin]))) > 0.05         # the rows carry real values
     assert float(np.max(np.abs(o[fin]))) > 0.05         # not the silent-zero failure
 

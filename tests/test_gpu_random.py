@@ -20,7 +20,8 @@ import torch
 
 from paged_kv_cache_173_amd import workloads as wl
 
-from gpu_common import Uploaded, compare, prefill_with_lengths, run_gpu, run_oracle, say
+from gpu_common import (Uploaded, assert_output_close, compare, prefill_with_lengths, run_gpu,
+                        run_oracle, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -208,8 +209,7 @@ def test_random_merge_states(pkv, case):
     vo, so = pkv.pkv_merge_states(v.cuda(), s.cuda())
     torch.cuda.synchronize()
     O, LSE = oracle.merge_states(v.double().numpy(), s.double().numpy())
-    tol = {torch.float16: 2e-3, torch.bfloat16: 1e-2, torch.float32: 1e-5}[dtype]
-    assert np.abs(vo.double().cpu().numpy() - O).max() <= tol
+    assert_output_close(vo, O, dtype, f"random merge_states {case}")
     fin = np.isfinite(LSE)
     so = so.cpu().numpy()
     assert np.array_equal(np.isneginf(so), ~fin)
