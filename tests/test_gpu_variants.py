@@ -232,6 +232,46 @@ def test_prefill_full_size_all_variants(pkv, ws):
                 label="full prefill, window+cap+sinks, every row")
 
 
+def _scaled_v(w, factor):
+    """w with every V entry multiplied by `factor` (then stored in the workload's format)."""
+    from extreme_inputs import _bits, _float
+    w.kv.v_cache = _bits(_float(w.kv.v_cache, w.dtype) * factor, w.dtype)
+    return w
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_one_key_rows_at_large_magnitudes(pkv, ws, dtype):
+    """A window of 0 keys: each row sees the key at its own position, whose weight is exactly
+    1, and a sink in the denominator, so a row's output is that V row times 1 / (1 + sink
+    weight), computed in fp32 and then stored in the 16-bit format. With V ~ N(0, 100) the
+    outputs reach the binades where half an ulp of the format exceeds the stated limit
+    (|O| >= 4 for bf16, >= 8 for fp16): the kernels must round to nearest there, since a
+    truncated conversion is off by up to a whole ulp, which the bound does not allow."""
+    limit = 4.0 if dtype == "bf16" else 8.0
+    for path in ("prefill", "decode"):
+        if path == "prefill":
+            qo = np.array([37, 64, 5])
+            w = prefill_with_lengths(seed=4242, qo_lens=qo, kv_lens=qo + np.array([0, 100, 3]),
+                                     Hq=8, Hkv=2, P=16, dtype=dtype)
+        else:
+            w = wl.batch_decode(seed=4243, kv_lens=[1, 17, 300, 64], num_qo_heads=8,
+                                num_kv_heads=2, page_size=16, dtype=dtype)
+        _scaled_v(w, 10.0)
+        sinks = _sinks(4244, 8, special=False)
+        run = run_prefill if path == "prefill" else run_decode
+        run(pkv, ws, w, W=0, sinks=sinks, label=f"one-key rows, {path}, {dtype}")
+        # the case reaches the coarse binades (checked on the oracle's side)
+        O, _ = (ov.batch_prefill_variant(w.q, w.kv.k_cache, w.kv.v_cache, w.qo_indptr,
+                                         w.kv.kv_indptr, w.kv.kv_indices, w.kv.last_page_len,
+                                         w.dtype, w.sm_scale, w.causal, window_left=0,
+                                         sinks=sinks)
+                if path == "prefill" else
+                ov.batch_decode_variant(w.q, w.kv.k_cache, w.kv.v_cache, w.kv.kv_indptr,
+                                        w.kv.kv_indices, w.kv.last_page_len, w.dtype,
+                                        w.sm_scale, window_left=0, sinks=sinks))
+        assert np.abs(O).max() > 2 * limit
+
+
 def test_no_variant_matches_plain_path(pkv, ws):
     """Window -1, cap 0 and no sinks select the plain kernels: the output is the same
     bits as a run without variant arguments."""
