@@ -60,7 +60,7 @@ def _check(pkv, ws, w, sched, label):
     compare(w, o, lse, O, LSE, label=label)
 
 
-@pytest.mark.parametrize("case", range(60))
+@pytest.mark.parametrize("case", range(120))
 def test_random_decode(pkv, ws, case):
     rng = np.random.default_rng(9100 + case)
     dtype = str(rng.choice(["f16", "bf16"]))
@@ -73,7 +73,7 @@ def test_random_decode(pkv, ws, case):
     _check(pkv, ws, w, _sched(rng), f"random decode {case} P={P} lens={list(lens)}")
 
 
-@pytest.mark.parametrize("case", range(120))
+@pytest.mark.parametrize("case", range(200))
 def test_random_prefill(pkv, ws, case):
     rng = np.random.default_rng(9300 + case)
     dtype = str(rng.choice(["f16", "bf16"]))
@@ -93,7 +93,7 @@ def test_random_prefill(pkv, ws, case):
            f"random prefill {case} P={P} causal={causal} qo={list(qo)} kv={list(kv)}")
 
 
-@pytest.mark.parametrize("case", range(40))
+@pytest.mark.parametrize("case", range(80))
 def test_random_cascade(pkv, ws, case):
     rng = np.random.default_rng(9500 + case)
     dtype = str(rng.choice(["f16", "bf16"]))
@@ -108,7 +108,7 @@ def test_random_cascade(pkv, ws, case):
            f"random cascade {case} P={P} prefix={prefix} suffix={list(sfx)}")
 
 
-@pytest.mark.parametrize("case", range(10))
+@pytest.mark.parametrize("case", range(30))
 def test_random_single_decode(pkv, ws, case):
     rng = np.random.default_rng(9700 + case)
     dtype = str(rng.choice(["f16", "bf16"]))
@@ -123,7 +123,7 @@ def test_random_single_decode(pkv, ws, case):
 # ----------------------------------------------------------------------------
 # the other entry points, with the helpers of their own test modules
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("case", range(32))
+@pytest.mark.parametrize("case", range(64))
 def test_random_block_sparse(pkv, ws, case):
     from test_gpu_block_sparse import check
     rng = np.random.default_rng(9900 + case)
@@ -142,7 +142,7 @@ def test_random_block_sparse(pkv, ws, case):
     check(pkv, ws, w, f"random block-sparse {case}")
 
 
-@pytest.mark.parametrize("case", range(8))
+@pytest.mark.parametrize("case", range(24))
 def test_random_append(pkv, case):
     from test_gpu_append import run_case
     rng = np.random.default_rng(10100 + case)
@@ -155,7 +155,7 @@ def test_random_append(pkv, case):
     run_case(pkv, w, f"random append {case}")
 
 
-@pytest.mark.parametrize("case", range(32))
+@pytest.mark.parametrize("case", range(112))
 def test_random_variants(pkv, ws, case):
     from test_gpu_variants import run_decode, run_prefill
     rng = np.random.default_rng(10300 + case)
@@ -181,7 +181,7 @@ def test_random_variants(pkv, ws, case):
                 label=f"random prefill variant {case}")
 
 
-@pytest.mark.parametrize("case", range(18))
+@pytest.mark.parametrize("case", range(40))
 def test_random_mixed_batch(pkv, ws, case):
     from test_gpu_pod import run_case
     rng = np.random.default_rng(10600 + case)
@@ -195,7 +195,7 @@ def test_random_mixed_batch(pkv, ws, case):
     run_case(pkv, ws, w, f"random mixed batch {case}", sched=_sched(rng))
 
 
-@pytest.mark.parametrize("case", range(6))
+@pytest.mark.parametrize("case", range(24))
 def test_random_merge_states(pkv, case):
     import oracle
     rng = np.random.default_rng(10800 + case)
